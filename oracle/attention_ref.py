@@ -1,0 +1,274 @@
+"""CPU oracle for the exact scaled-dot-product attention forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only the tests, the package's smoke check and the
+bench's CPU-baseline leg use it.  It shares no code with the HIP kernels.
+
+Sources (web pages; cited by title and section):
+
+* [G]  "FlashAttention算法详解：从IO瓶颈到Triton实现" (gentlecold.top)
+* [Y]  FlashAttention paper walkthrough, flash_attention.zh (youngju.dev)
+* [F]  "FlashAttention 完整解析：从原理到 CUDA/Triton 实现" (freezetheflame.cc)
+
+What is computed (the plain definition, fp64 throughout):
+
+    O = softmax(scale * Q K^T + M) V                      [G] 先说结论 (the equation)
+    LSE_r = m_r + ln l_r                                   [G] Backward为什么更复杂
+
+for every batch entry b and head h, with the additive mask M equal to 0 on
+the visible key set J_r of query row r and -inf elsewhere:
+
+    J_r = { c : c < N,
+                c <= r          if causal           [G] Causal Mask怎么处理
+                c < kv_len[b]   if key padding }    [G] FlashAttention Forward流程 ("padding")
+
+The softmax is the max-subtracted ("safe") form of [G] Online Softmax and
+[Y] §6.1.  The oracle materialises S and P, one block of query rows at a
+time (the full N x N never fits at N = 65536); the row blocking only bounds
+memory and does not change any row's arithmetic.  The two products are
+plain BLAS matrix products.
+
+Readings where the pages are silent (each is also listed in the design
+notes):
+
+* A row with no visible key (kv_len = 0) has O_r = 0 and LSE_r = -inf.
+* ``scale`` is used as the float32 value a kernel receives, widened to
+  float64.
+* LSE is in natural-log units of the scaled logits.
+
+``online_attention_ref`` follows the blocked online-softmax recurrence of
+[G] Online Softmax / FlashAttention Forward流程 and [Y] §6.2 in fp64, with an
+arbitrary key-block partition and visiting order; it exists to pin the
+recurrence (the worked example, block-order independence), not for parity.
+``brute_ref`` is the same definition as scalar Python loops with
+``math.exp``/``math.fsum`` for tiny shapes.
+"""
+from __future__ import annotations
+
+import math
+from concurrent.futures import ThreadPoolExecutor
+from typing import Iterable, List, Optional, Sequence
+
+import numpy as np
+
+MASK_NONE = 0
+MASK_CAUSAL = 1
+MASK_KEY_PADDING = 2
+
+
+def _as_scale(scale: float) -> float:
+    return float(np.float32(scale))
+
+
+def _kv_len(mask_kind: int, kv_lens, b: int, N: int) -> int:
+    if mask_kind & MASK_KEY_PADDING:
+        return max(0, min(int(kv_lens[b]), N))
+    return N
+
+
+def _head_ref(qh, kh, vh, scale, causal, n_vis, rows, row_block):
+    """Definition of O and LSE for one (b, h) over the query rows ``rows``."""
+    d = vh.shape[1]
+    out = np.zeros((len(rows), d), dtype=np.float64)
+    lse = np.full(len(rows), -np.inf, dtype=np.float64)
+    for start in range(0, len(rows), row_block):
+        rr = rows[start:start + row_block]
+        kmax = min(n_vis, int(rr.max()) + 1) if causal else n_vis
+        if kmax <= 0:
+            continue
+        # S = scale * Q K^T on the keys that can be visible to this block.
+        s = (qh[rr] @ kh[:kmax].T) * scale
+        if causal:
+            cols = np.arange(kmax)
+            s[cols[None, :] > rr[:, None]] = -np.inf
+        m = s.max(axis=1)
+        ok = np.isfinite(m)                      # rows with >= 1 visible key
+        p = np.exp(s[ok] - m[ok, None])          # exp(S - rowmax), masked -> 0
+        l = p.sum(axis=1)
+        idx = start + np.nonzero(ok)[0]
+        out[idx] = (p @ vh[:kmax]) / l[:, None]  # P V with P = p / l
+        lse[idx] = m[ok] + np.log(l)
+    return out, lse
+
+
+def attention_ref(q, k, v, scale, mask_kind=MASK_NONE, kv_lens=None,
+                  rows: Optional[Sequence[int]] = None, heads=None,
+                  row_block: int = 512, workers: int = 1):
+    """fp64 O and LSE of exact attention.
+
+    q, k, v: float64 arrays ``[B, H, N, d]`` (callers widen the generated
+    bf16/fp32 data exactly).  ``rows``: optional sorted query-row indices to
+    compute (default: all).  ``heads``: optional list of (b, h) pairs
+    (default: all).  Returns ``O [B, H, R, d]`` and ``LSE [B, H, R]``; rows
+    of heads not requested are left NaN.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, N, d = q.shape
+    if k.shape != (B, H, N, d) or v.shape != (B, H, N, d):
+        raise ValueError("q, k, v must share the shape [B, H, N, d]")
+    if mask_kind & ~(MASK_CAUSAL | MASK_KEY_PADDING):
+        raise ValueError(f"unknown mask bits in {mask_kind}")
+    if (mask_kind & MASK_KEY_PADDING) and kv_lens is None:
+        raise ValueError("key padding needs kv_lens")
+    scale = _as_scale(scale)
+    causal = bool(mask_kind & MASK_CAUSAL)
+    rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
+    units = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
+    O = np.full((B, H, len(rows), d), np.nan)
+    L = np.full((B, H, len(rows)), np.nan)
+
+    def run(unit):
+        b, h = unit
+        n_vis = _kv_len(mask_kind, kv_lens, b, N)
+        O[b, h], L[b, h] = _head_ref(q[b, h], k[b, h], v[b, h], scale, causal,
+                                     n_vis, rows, row_block)
+
+    if workers <= 1 or len(units) == 1:
+        for u in units:
+            run(u)
+    else:
+        # Parallel over independent heads only; each head's arithmetic is the
+        # same as in the serial loop.  BLAS is held to one thread per worker.
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(1), ThreadPoolExecutor(workers) as ex:
+            list(ex.map(run, units))
+    return O, L
+
+
+def probabilities_ref(q, k, scale, mask_kind=MASK_NONE, kv_lens=None, b=0, h=0):
+    """The full fp64 probability matrix P of one head (small N only)."""
+    q = np.asarray(q, dtype=np.float64)[b, h]
+    k = np.asarray(k, dtype=np.float64)[b, h]
+    N = q.shape[0]
+    s = (q @ k.T) * _as_scale(scale)
+    vis = np.ones((N, N), dtype=bool)
+    if mask_kind & MASK_CAUSAL:
+        vis &= np.arange(N)[None, :] <= np.arange(N)[:, None]
+    if mask_kind & MASK_KEY_PADDING:
+        vis &= np.arange(N)[None, :] < _kv_len(mask_kind, kv_lens, b, N)
+    s = np.where(vis, s, -np.inf)
+    m = s.max(axis=1)
+    P = np.zeros_like(s)
+    ok = np.isfinite(m)
+    e = np.exp(s[ok] - m[ok, None])
+    P[ok] = e / e.sum(axis=1, keepdims=True)
+    return P
+
+
+# ---------------------------------------------------------------------------
+# The online (blocked) recurrence, in the pages' notation.
+# ---------------------------------------------------------------------------
+
+def online_softmax_stats(x: Sequence[float], blocks: Sequence[Sequence[int]]):
+    """Running (m, l) of one logit row, visiting key blocks in the given order.
+
+    Per block:  m_new = max(m, max(block));
+                l_new = l * exp(m - m_new) + sum_{j in block} exp(x_j - m_new)
+    ([G] Online Softmax; [Y] §6.2).  Returns the list of (m, l) after each
+    block, starting from m = -inf, l = 0.
+    """
+    m, l = -math.inf, 0.0
+    trace = []
+    for blk in blocks:
+        vals = [float(x[j]) for j in blk]
+        m_new = max([m] + vals)
+        if m_new == -math.inf:
+            trace.append((m, l))
+            continue
+        alpha = math.exp(m - m_new) if m != -math.inf else 0.0
+        l = l * alpha + math.fsum(math.exp(t - m_new) for t in vals)
+        m = m_new
+        trace.append((m, l))
+    return trace
+
+
+def partition(N: int, block: int) -> List[np.ndarray]:
+    """Split key indices 0..N-1 into consecutive blocks of ``block`` keys."""
+    return [np.arange(s, min(N, s + block)) for s in range(0, N, block)]
+
+
+def online_attention_ref(q, k, v, scale, mask_kind=MASK_NONE, kv_len=None,
+                         blocks: Optional[Iterable[np.ndarray]] = None):
+    """One head's O and LSE by the blocked online-softmax loop, in fp64.
+
+    q, k, v: ``[N, d]`` float64.  ``blocks``: key-index blocks in visiting
+    order (any partition of 0..N-1, any order).  Every query row is carried
+    through the same loop ([G] FlashAttention Forward流程):
+
+        qk    = scale * Q K_j^T, masked to -inf
+        m_new = max(m, rowmax(qk))
+        p     = exp(qk - m_new);  alpha = exp(m - m_new)
+        acc   = alpha * acc + p V_j;  l = alpha * l + rowsum(p);  m = m_new
+        O = acc / l;  LSE = m + ln l
+
+    Rows whose running max is still -inf use 0 in place of m_new, so their p
+    is 0 (masked) and alpha is irrelevant (acc and l are still 0).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    N, d = q.shape
+    scale = _as_scale(scale)
+    if blocks is None:
+        blocks = partition(N, 64)
+    n_vis = N if kv_len is None else max(0, min(int(kv_len), N))
+    rows = np.arange(N)
+    m = np.full(N, -np.inf)
+    l = np.zeros(N)
+    acc = np.zeros((N, d))
+    for cols in blocks:
+        cols = np.asarray(cols, dtype=np.int64)
+        qk = (q @ k[cols].T) * scale
+        vis = np.ones(qk.shape, dtype=bool)
+        if mask_kind & MASK_CAUSAL:
+            vis &= cols[None, :] <= rows[:, None]
+        if mask_kind & MASK_KEY_PADDING:
+            vis &= cols[None, :] < n_vis
+        qk = np.where(vis, qk, -np.inf)
+        m_new = np.maximum(m, qk.max(axis=1))
+        base = np.where(np.isfinite(m_new), m_new, 0.0)
+        p = np.exp(qk - base[:, None])
+        alpha = np.where(np.isfinite(m), np.exp(m - base), 0.0)
+        acc = alpha[:, None] * acc + p @ v[cols]
+        l = alpha * l + p.sum(axis=1)
+        m = m_new
+    out = np.zeros((N, d))
+    lse = np.full(N, -np.inf)
+    ok = l > 0
+    out[ok] = acc[ok] / l[ok, None]
+    lse[ok] = m[ok] + np.log(l[ok])
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# Scalar brute force for tiny shapes.
+# ---------------------------------------------------------------------------
+
+def brute_ref(q, k, v, scale, mask_kind=MASK_NONE, kv_lens=None):
+    """Pure-Python loops of the definition (math.exp, math.fsum); tiny N only."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, N, d = q.shape
+    scale = _as_scale(scale)
+    O = np.zeros((B, H, N, d))
+    L = np.full((B, H, N), -np.inf)
+    for b in range(B):
+        n_vis = _kv_len(mask_kind, kv_lens, b, N)
+        for h in range(H):
+            for r in range(N):
+                J = [c for c in range(N)
+                     if c < n_vis and (not (mask_kind & MASK_CAUSAL) or c <= r)]
+                if not J:
+                    continue
+                s = {c: scale * math.fsum(float(q[b, h, r, t]) * float(k[b, h, c, t])
+                                          for t in range(d)) for c in J}
+                mx = max(s.values())
+                e = {c: math.exp(s[c] - mx) for c in J}
+                den = math.fsum(e.values())
+                for t in range(d):
+                    O[b, h, r, t] = math.fsum(e[c] * float(v[b, h, c, t]) for c in J) / den
+                L[b, h, r] = mx + math.log(den)
+    return O, L

@@ -1,0 +1,58 @@
+"""The seeded input generator: reproducible, correctly encoded, right shapes."""
+import numpy as np
+import pytest
+
+from fa_inputs import (MASK_CAUSAL, MASK_KEY_PADDING, WORKLOADS, bf16_bits_to_f32,
+                       f32_to_bf16_bits, make_inputs, make_raw, to_f64)
+
+
+def test_reproducible_from_seed():
+    a = make_raw(1, 2, 33, 8, "bf16", seed=7, kv_len_range=(3, 9))
+    b = make_raw(1, 2, 33, 8, "bf16", seed=7, kv_len_range=(3, 9))
+    c = make_raw(1, 2, 33, 8, "bf16", seed=8, kv_len_range=(3, 9))
+    for n in "qkv":
+        assert np.array_equal(a[n], b[n])
+        assert not np.array_equal(a[n], c[n])
+    assert np.array_equal(a["kv_lens"], b["kv_lens"])
+
+
+def test_bf16_rne_matches_torch():
+    torch = pytest.importorskip("torch")
+    g = np.random.default_rng(0)
+    x = np.concatenate([g.standard_normal(100000).astype(np.float32) * 10,
+                        np.array([0.0, -0.0, 1.0, 1.00390625, 1.01171875, 3e38, -3e38,
+                                  1e-40, np.inf, -np.inf], dtype=np.float32)])
+    ours = f32_to_bf16_bits(x)
+    theirs = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, theirs)
+    # Ties go to even: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7.
+    assert f32_to_bf16_bits(np.array([1.00390625], np.float32))[0] == 0x3F80
+    assert np.array_equal(bf16_bits_to_f32(ours[:100]).view(np.uint32) >> 16, ours[:100])
+
+
+def test_workload_shapes_and_recipe():
+    wl = WORKLOADS["bf16_b8h16_n2048_d64_keypad"]
+    x = make_inputs(wl)
+    assert x["q"].shape == (8, 16, 2048, 64) and x["q"].dtype == np.uint16
+    assert x["kv_lens"].dtype == np.int32 and x["kv_lens"].shape == (8,)
+    assert ((x["kv_lens"] >= 1024) & (x["kv_lens"] <= 2048)).all()
+    assert wl.mask_kind == MASK_KEY_PADDING
+    f = WORKLOADS["f32_b1h1_n256_d64"]
+    y = make_inputs(f)
+    assert y["q"].dtype == np.float32 and y["kv_lens"] is None
+    assert abs(f.scale - 0.125) == 0.0
+
+
+def test_q_multiplier_is_exact():
+    a = make_raw(1, 1, 64, 16, "f32", seed=3, q_mult=1.0)
+    b = make_raw(1, 1, 64, 16, "f32", seed=3, q_mult=2.0)
+    assert np.array_equal(b["q"], a["q"] * 2)
+    assert np.array_equal(b["k"], a["k"])
+
+
+def test_flop_formula():
+    wl = WORKLOADS["bf16_b2h32_n4096_d128_causal"]
+    assert wl.mask_kind == MASK_CAUSAL
+    assert wl.flops() == 4 * 2 * 32 * 4096 * 4096 * 128 / 2
+    assert abs(wl.scale - 1 / np.sqrt(128)) < 1e-8
+    assert to_f64(np.array([0x3F80], np.uint16))[0] == 1.0
