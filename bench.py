@@ -1,0 +1,183 @@
+#!/usr/bin/env python3
+"""Throughput of the exact attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one fa_fwd call over the whole batch of the workload (default:
+B=2, H=32, N=4096, d=128, bf16, causal), inputs already resident in device
+memory.  Prints ONE JSON line with the throughput (FLOPs by 4*B*H*N^2*d,
+halved for causal), the roofline figures of the kernel, and the CPU oracle
+timed on the host as a reported baseline.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fwd attention TFLOP/s (bf16, N=4096 d=128 causal) and % of MFMA peak"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA peaks
+KERNEL_SRC = os.path.join(ROOT, "exact_attention_92_amd", "csrc", "fa_fwd.hip")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "fa_fwd_bf16_b2h32_n4096_d128_causal_pmc.md")
+
+
+def kernel_source_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed PMC summary, if it was taken on
+    the current kernel source; otherwise None."""
+    try:
+        text = open(PMC_SUMMARY).read()
+    except OSError:
+        return None
+    m = re.search(r"```json\s*(\{.*?\})\s*```", text, re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(x, wl, o_gpu):
+    """Time the oracle on the host (all heads of the workload) and check the
+    GPU output against it on the same bytes."""
+    from fa_inputs import to_f64
+    from oracle import attention_ref
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    q, k, v = (to_f64(x[n]) for n in "qkv")
+    t0 = time.perf_counter()
+    Or, Lr = attention_ref(q, k, v, wl.scale, wl.mask_kind, x["kv_lens"], workers=cores)
+    dt = time.perf_counter() - t0
+    err = np.abs(o_gpu - Or)
+    parity = {"o_max_abs": float(err.max()),
+              "o_rel_frobenius": float(np.linalg.norm(o_gpu - Or) / np.linalg.norm(Or))}
+    return {"value": wl.flops() / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"the whole workload ({wl.B * wl.H} heads, all rows), fp64 NumPy/BLAS, "
+                      f"{cores} worker threads with single-threaded BLAS"}, parity
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="first run 3 plain device copies of this many MiB (a known-size "
+                         "reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the attention forward here runs on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_attention_92_amd as fa
+    from fa_inputs import BENCH_WORKLOAD, WORKLOADS, bf16_bits_to_f32, make_inputs
+
+    if args.copy_mib > 0:
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    wl = WORKLOADS[args.workload or BENCH_WORKLOAD]
+    x = make_inputs(wl)
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    q, k, v = up(x["q"]), up(x["k"]), up(x["v"])
+    kv = None if x["kv_lens"] is None else torch.from_numpy(x["kv_lens"]).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((wl.B, wl.H, wl.N), dtype=torch.float32, device=dev)
+    fn = fa.fa_fwd if wl.dtype == "bf16" else fa.fa_fwd_f32
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        fn(q, k, v, o, lse, wl.scale, wl.mask_kind, kv, stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: K steps; an event pair around every launch on the launch
+    # stream gives the per-launch kernel duration as well.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    launch_ms = [a.elapsed_time(b) for a, b in evs]
+    ms_per_step = total_ms / args.steps
+    avg_launch_ms = float(np.mean(launch_ms))
+
+    flops = wl.flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[wl.dtype]
+    achieved = flops / (avg_launch_ms * 1e-3) / 1e12
+    traffic = measured_traffic() if wl.name == BENCH_WORKLOAD else None
+    rec = {
+        "metric": METRIC if wl.name == BENCH_WORKLOAD else f"fwd attention TFLOP/s ({wl.name})",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d,
+                   "mask": {0: "none", 1: "causal", 2: "key_padding"}[wl.mask_kind],
+                   "scale": wl.scale, "q_mult": wl.q_mult, "seed": wl.seed,
+                   "flops_per_step": flops, "device": torch.cuda.get_device_name(dev)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "kernel": "fa_fwd_bf16_kernel" if wl.dtype == "bf16" else "fa_fwd_f32_kernel",
+                     "avg_launch_us": round(avg_launch_ms * 1e3, 2),
+                     "min_launch_us": round(min(launch_ms) * 1e3, 2)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        if wl.dtype == "bf16":
+            bits = o.view(torch.int16).cpu().numpy().view(np.uint16)
+            o_host = bf16_bits_to_f32(bits).astype(np.float64)
+        else:
+            o_host = o.cpu().numpy().astype(np.float64)
+        rec["cpu_baseline"], rec["parity_vs_oracle"] = cpu_baseline(x, wl, o_host)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,100 @@
+/*
+ * fa_api.h -- C ABI of the exact attention forward library (libfa92.so).
+ *
+ * What the library computes, for every batch entry b and head h:
+ *
+ *     O   = softmax(scale * Q K^T + M) V
+ *     LSE = m + ln(l)        (per query row: row max m and row sum l of the
+ *                             exponentials of the scaled, masked logits)
+ *
+ * This is the exact scaled-dot-product attention of "FlashAttention算法详解：
+ * 从IO瓶颈到Triton实现" (gentlecold.top), section 先说结论 (the equation), with
+ * LSE as in its section Backward为什么更复杂.  It is computed IO-aware: each
+ * block of query rows streams over blocks of keys and values with the
+ * online-softmax state (running max, running sum, rescaled accumulator) of
+ * that page's sections Online Softmax and FlashAttention Forward流程, so the
+ * N x N scores and probabilities never reach device memory.
+ *
+ * Conventions shared by both entry points:
+ *
+ *  - q, k, v, o: DEVICE pointers to contiguous row-major tensors of shape
+ *    [B, H, N, d] (batch, head, sequence, head dimension).  Element type is
+ *    bfloat16 for fa_fwd and float32 for fa_fwd_f32; o has the input type.
+ *    Every pointer must be 16-byte aligned.  Self-attention: queries and keys
+ *    share the length N.
+ *  - lse: DEVICE pointer to float32 [B, H, N], natural-log units of the
+ *    scaled logits.  A query row with no visible key gets O = 0 and
+ *    LSE = -inf.
+ *  - B, H, N >= 1; d is 64 or 128.  B * H * ceil(N / 128) must not exceed
+ *    2^31 - 1.
+ *  - scale: any finite float; the logits are scale * q.k.  (1/sqrt(d) is the
+ *    usual value.)  |scale| below 1e-30 is treated as 1e-30, which gives the
+ *    same uniform softmax as scale = 0 to within float32 rounding.
+ *  - mask_kind: bit flags.  FA_MASK_CAUSAL hides key c from query r when
+ *    c > r (the diagonal stays visible; "Causal Mask怎么处理" on the page
+ *    above).  FA_MASK_KEY_PADDING hides keys c >= kv_lens[b] from every
+ *    query row and head of batch entry b.  Both flags: the union of the
+ *    hidden sets.  Other bits are rejected.
+ *  - kv_lens: DEVICE pointer to int32 [B], required when FA_MASK_KEY_PADDING
+ *    is set, ignored (may be NULL) otherwise.  Values are read on the device
+ *    and clamped to [0, N].
+ *  - stream: a hipStream_t (NULL = the default stream).  The call enqueues
+ *    one kernel on it and returns without synchronising.
+ *
+ * Ownership and side effects: the caller owns every buffer; the library
+ * allocates no memory and keeps no state.  It writes o and lse and nothing
+ * else.  Inputs are only read.
+ *
+ * Errors: every argument is checked on the host before anything is
+ * enqueued; on an error the call returns a negative status and writes
+ * nothing.  FA_ERR_HIP reports a launch failure (from hipGetLastError).
+ * Faults that happen while the kernel runs surface at the caller's next
+ * synchronisation, as with any asynchronous launch.
+ */
+#ifndef FA_API_H
+#define FA_API_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  FA_MASK_NONE = 0,
+  FA_MASK_CAUSAL = 1,
+  FA_MASK_KEY_PADDING = 2
+};
+
+enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size, bad mask bits,
+                              non-finite scale, padding without kv_lens */
+  FA_ERR_UNSUPPORTED = -2, /* head dimension d other than 64 or 128 */
+  FA_ERR_HIP = -3          /* the kernel launch failed */
+};
+
+/* bfloat16 forward.  q, k, v, o: bf16 [B, H, N, d]; lse: float32 [B, H, N].
+ * Products run on the bf16 matrix cores with float32 accumulation; the
+ * probabilities are rounded to bf16 before they multiply V (as the pages'
+ * Triton sketch does with p.to(v.dtype)); O is rounded to bf16 (nearest,
+ * ties to even) once, at the end. */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int mask_kind,
+           const int32_t* kv_lens, void* stream);
+
+/* float32 forward: same contract with float32 q, k, v, o.  Every product and
+ * sum is float32 (matrix-core fp32 multiply-accumulate); nothing is rounded
+ * to a narrower type. */
+int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int d, float scale, int mask_kind,
+               const int32_t* kv_lens, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* fa_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_API_H */

@@ -1,0 +1,78 @@
+"""Helpers shared by the GPU parity tests (upload, run, compare)."""
+import sys
+
+import numpy as np
+
+from fa_inputs import bf16_bits_to_f32
+
+# Tolerances.  fp32: O max-abs 1e-4.  bf16 inputs with fp32 accumulation:
+# O max-abs 1e-2 and relative Frobenius 5e-3.  LSE: 1e-4 (fp32) and 1e-3
+# (bf16); rows with no visible key must give LSE = -inf and O = 0 exactly.
+TOL = {
+    "f32": {"o_abs": 1e-4, "o_relf": None, "lse_abs": 1e-4},
+    "bf16": {"o_abs": 1e-2, "o_relf": 5e-3, "lse_abs": 1e-3},
+}
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a):
+    import torch
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def run_gpu(x, scale, mask_kind, sentinel=True):
+    """Upload generated inputs, run the matching entry point, return fp64 O, LSE."""
+    import torch
+
+    import exact_attention_92_amd as fa
+    q, k, v = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"])
+    kv = None
+    if x.get("kv_lens") is not None:
+        kv = torch.from_numpy(np.asarray(x["kv_lens"], dtype=np.int32)).cuda()
+    B, H, N, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if sentinel:
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+    fn = fa.fa_fwd if q.dtype == torch.bfloat16 else fa.fa_fwd_f32
+    fn(q, k, v, o, lse, scale, mask_kind, kv)
+    torch.cuda.synchronize()
+    return o_to_f64(o), lse.cpu().numpy().astype(np.float64)
+
+
+def o_to_f64(o):
+    import torch
+    if o.dtype == torch.bfloat16:
+        bits = o.view(torch.int16).cpu().numpy().view(np.uint16)
+        return bf16_bits_to_f32(bits).astype(np.float64)
+    return o.cpu().numpy().astype(np.float64)
+
+
+def compare(O, L, Or, Lr, dtype, what=""):
+    """Assert parity of O and LSE against the oracle; returns the error stats."""
+    tol = TOL[dtype]
+    assert not np.isnan(O).any(), f"{what}: O has unwritten (NaN) elements"
+    assert not np.isnan(L).any(), f"{what}: LSE has unwritten (NaN) elements"
+    empty = ~np.isfinite(Lr)
+    assert np.array_equal(~np.isfinite(L), empty), f"{what}: LSE -inf pattern differs"
+    if empty.any():
+        assert np.all(L[empty] == -np.inf) and np.all(O[empty] == 0.0), f"{what}: empty rows"
+    err = np.abs(O - Or)
+    stats = {"o_abs": float(err.max(initial=0.0))}
+    nrm = np.linalg.norm(Or)
+    stats["o_relf"] = float(np.linalg.norm(O - Or) / nrm) if nrm > 0 else 0.0
+    stats["lse_abs"] = float(np.abs(L[~empty] - Lr[~empty]).max(initial=0.0))
+    say(f"  {what}: max|dO|={stats['o_abs']:.3e} relF={stats['o_relf']:.3e} "
+        f"max|dLSE|={stats['lse_abs']:.3e}")
+    assert stats["o_abs"] <= tol["o_abs"], (what, stats)
+    if tol["o_relf"] is not None:
+        assert stats["o_relf"] <= tol["o_relf"], (what, stats)
+    assert stats["lse_abs"] <= tol["lse_abs"], (what, stats)
+    return stats

@@ -1,0 +1,87 @@
+"""The C-ABI library: it loads, exports every declared symbol, and rejects bad
+arguments on the host before anything is enqueued (no GPU needed: no call
+here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa_api.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import exact_attention_92_amd as fa
+    if not os.path.exists(fa.LIB_PATH):
+        pytest.fail("libfa92.so is not built (run __graft_entry__.build())")
+    return fa.load_library()
+
+
+def test_header_declares_the_entry_points():
+    assert _declared() == ["fa_fwd", "fa_fwd_f32", "fa_strerror"]
+
+
+def test_library_exports_every_declared_symbol(lib):
+    import exact_attention_92_amd as fa
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert tuple(sorted(fa.EXPORTS)) == tuple(_declared())
+
+
+def test_strerror(lib):
+    import exact_attention_92_amd as fa
+    assert fa.fa_strerror(0) == "ok"
+    for st in (fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_HIP, 12345):
+        assert isinstance(fa.fa_strerror(st), str) and fa.fa_strerror(st)
+
+
+def _call(lib, name, ptrs=(0x1000, 0x2000, 0x3000, 0x4000, 0x5000), B=1, H=1, N=16, d=64,
+          scale=0.125, mask=0, kv=None):
+    fn = getattr(lib, name)
+    return fn(*[ctypes.c_void_p(p) if p is not None else None for p in ptrs], B, H, N, d,
+              ctypes.c_float(scale), mask, ctypes.c_void_p(kv) if kv else None, None)
+
+
+@pytest.mark.parametrize("name", ["fa_fwd", "fa_fwd_f32"])
+def test_invalid_arguments_are_rejected_before_launch(lib, name):
+    import exact_attention_92_amd as fa
+    bad = fa.FA_ERR_INVALID_ARG
+    assert _call(lib, name, ptrs=(None, 0x2000, 0x3000, 0x4000, 0x5000)) == bad
+    assert _call(lib, name, ptrs=(0x1000, 0x2000, 0x3000, 0x4000, None)) == bad
+    assert _call(lib, name, ptrs=(0x1008, 0x2000, 0x3000, 0x4000, 0x5000)) == bad  # misaligned
+    assert _call(lib, name, ptrs=(0x1000, 0x2000, 0x3000, 0x4004, 0x5000)) == bad
+    assert _call(lib, name, B=0) == bad
+    assert _call(lib, name, H=-1) == bad
+    assert _call(lib, name, N=0) == bad
+    assert _call(lib, name, mask=4) == bad
+    assert _call(lib, name, mask=fa.FA_MASK_KEY_PADDING) == bad  # padding without kv_lens
+    assert _call(lib, name, scale=float("nan")) == bad
+    assert _call(lib, name, scale=float("inf")) == bad
+    assert _call(lib, name, B=1 << 20, H=1 << 10, N=1 << 20) == bad  # grid too large
+    assert _call(lib, name, d=96) == fa.FA_ERR_UNSUPPORTED
+    assert _call(lib, name, d=256) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    import exact_attention_92_amd as fa
+    monkeypatch.setattr(fa, "_lib", None)
+    monkeypatch.setattr(fa, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        fa.load_library()
+
+
+def test_product_path_does_not_reach_the_oracle():
+    pkg = os.path.join(ROOT, "exact_attention_92_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert "oracle" not in text.replace("oracle_", ""), fn
