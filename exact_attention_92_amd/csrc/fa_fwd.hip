@@ -11,32 +11,40 @@
 // FlashAttention-2 order of §4.3 of "FlashAttention 完整解析" on
 // freezetheflame.cc: queries outside, keys inside, normalise last).
 //
-// Mapping to CDNA4 (design notes in the repository describe the choices):
+// Mapping to CDNA4 (the design notes of the repository give the measurements
+// behind each choice):
 //
-//  * One workgroup = 4 wavefronts = one block of 32*QW*4 query rows of one
-//    (batch, head).  Each wave owns 32*QW query rows; the wave's rows are the
-//    N dimension of a 32x32 MFMA tile.  K/V blocks of 64 keys are shared by
-//    the 4 waves through LDS (double buffered, prefetched into registers one
-//    block ahead).
+//  * One workgroup = 4 wavefronts = one block of 128 query rows of one
+//    (batch, head); each wave owns 32 rows, the N dimension of a 32x32 MFMA
+//    tile.  Two workgroups share a CU (2 waves per SIMD), so one wave's
+//    MFMAs overlap the other's softmax.  Blocks of 64 keys are staged through
+//    LDS, double buffered: raw buffer loads bring block j+1 into registers
+//    while block j is computed (rows past the end read as zero).
 //  * Scores are computed transposed, S^T = K Q^T, with
-//    v_mfma_f32_32x32x16_bf16: the accumulator then holds ONE query per lane
+//    v_mfma_f32_32x32x16_bf16: the accumulator holds ONE query row per lane
 //    (lane % 32) and 16 keys per lane, so the softmax row statistics are
-//    per-lane scalars plus one exchange between lanes l and l^32.
+//    per-lane scalars plus one exchange between lanes l and l^32
+//    (v_permlane32_swap).
 //  * The K rows fed to the MFMA are permuted (bits 2 and 3 of the row index
-//    swapped) so that each lane's 8 consecutive accumulator registers hold 8
-//    CONSECUTIVE keys.  Those registers, rounded to bf16, are directly the B
-//    operand of O^T = V^T P^T; V is stored transposed in LDS so the A operand
-//    is one 16-byte LDS read per lane.  P never leaves registers.
+//    swapped) so each lane's 8 consecutive accumulator registers hold 8
+//    CONSECUTIVE keys.  Rounded to bf16 they are directly the B operand of
+//    O^T = V^T P^T; P never leaves registers.  V is transposed on its way
+//    into LDS (v_perm_b32 regrouping, 8-byte stores) so the A operand of
+//    every P V MFMA is one 16-byte ds_read_b128; on gfx950 that read moves
+//    twice the bytes per clock of the ds_read_b64_tr_b16 transpose read.
 //  * Scores are kept in log2 units (scale * log2(e) folded into one FMA) and
 //    exponentiated with v_exp_f32 (a native 2^x).  The probabilities are
 //    rounded to bf16 for the P V product.  Two row sums are kept: one over
 //    the rounded values (v_dot2c_f32_bf16 against 1.0) normalises O, so the
 //    weights applied to V sum to exactly 1; the fp32 one gives LSE.
-//  * The running max is only moved when a block's max exceeds it by more than
-//    TAU (log2 units); the exponentials are then bounded by 2^TAU and most
-//    blocks skip the accumulator rescale.  Any reference point gives the
+//  * The running max is a reference point that moves only when it must: a
+//    wave's first block sets it from the block's row max; later blocks
+//    exponentiate against it directly, and only when a row sum shows a
+//    probability above 2^20 (or an infinite one) is the block redone with a
+//    fresh row max and the state rescaled.  Any reference point gives the
 //    same softmax (the rescaling identity of the online-softmax section of
-//    the youngju.dev walkthrough, §6.3), so this is exact up to rounding.
+//    the youngju.dev walkthrough, §6.3), so this is exact up to rounding; it
+//    removes the per-block row-max reduction and almost every rescale.
 //  * Causal: key blocks above the workgroup's last row are never loaded;
 //    a wave skips the blocks above its own rows; only blocks that cross the
 //    diagonal, the key-padding edge or the sequence end are masked
@@ -62,10 +70,10 @@ typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBN = 64;              // keys per block (bf16 kernel)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kTau = 8.0f;         // max-move threshold, log2 units
+constexpr float kOverflowSum = 1048576.f;  // 2^20: largest block row sum kept on the fast path
+constexpr float kTau = 8.0f;         // fp32 kernel: max-move threshold, log2 units
 constexpr float kMinScale = 1e-30f;
 
 __device__ __forceinline__ f32x16_t mfma_bf16(u32x4_t a, u32x4_t b, f32x16_t c) {
@@ -98,9 +106,20 @@ __device__ __forceinline__ float sum_bf16x2(unsigned pair, float acc) {
                                          __builtin_bit_cast(bf16x2_t, 0x3f803f80u), acc, false);
 }
 
+// Raw buffer resource over [base, base + bytes): loads past the end return 0.
+// Word 3 selects the raw 32-bit data format used by CDNA buffer loads.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4_t buf_load16(rsrc_t r, uint32_t voff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+}
+
 // Row of K that MFMA row m reads: bits 2 and 3 of m swapped.  With it, the
 // accumulator register r of lane-half h holds key 16*(r/8) + 8*h + (r%8) of
-// each 32-key tile.
+// each 32-key tile, so 8 consecutive registers are 8 consecutive keys.
 __device__ __forceinline__ int k_row_perm(int m) {
   return (m & 0x13) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
@@ -138,21 +157,25 @@ struct Params {
 #define FA_WAVES_PER_EU 2
 #endif
 
-template <int D, int QW>
+
+template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FA_WAVES_PER_EU)))
 void fa_fwd_bf16_kernel(Params p) {
-  constexpr int BM = 32 * QW * kWaves;
+  constexpr int BN = 64;            // keys per block
+  constexpr int BM = 32 * kWaves;   // query rows per workgroup
   constexpr int KS = D / 16;        // MFMA k-steps over d for S^T
   constexpr int DT = D / 32;        // 32-row tiles of O^T
-  constexpr int KT = kBN / 32;      // 32-key tiles of S^T
-  constexpr int PC = kBN / 16;      // 16-key chunks of P^T
+  constexpr int KT = BN / 32;       // 32-key tiles of S^T
+  constexpr int PC = BN / 16;       // 16-key chunks of P^T
   constexpr int KLD = D + 8;        // K row stride in LDS (elements)
-  constexpr int VLD = kBN + 8;      // V^T row stride in LDS (elements)
-  constexpr int KU = kBN * (D / 8) / kThreads;   // 16-byte K pieces per thread
-  constexpr int VUNITS = (kBN / 4) * (D / 8);    // 4-key x 8-d V pieces
-  static_assert(KU >= 1 && VUNITS <= kThreads, "tile shape");
+  constexpr int VLD = BN + 8;       // V^T row stride in LDS (elements)
+  constexpr uint32_t ROWB = D * 2;  // bytes per row in device memory
+  constexpr int CPR = D / 8;        // 16-byte chunks per row
+  constexpr int KU = BN * CPR / kThreads;    // 16-byte K pieces per thread
+  constexpr int VUNITS = (BN / 4) * CPR;     // V pieces of 4 keys x 8 dims
+  static_assert(KU >= 1 && (BN * CPR) % kThreads == 0 && VUNITS <= kThreads, "tile shape");
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kBN][KLD];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BN][KLD];
   __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][D][VLD];
 
   const int tid = threadIdx.x;
@@ -167,9 +190,9 @@ void fa_fwd_bf16_kernel(Params p) {
   map_block(p.nqb, causal, bh, qb);
   const int b = bh / p.H;
   const size_t hoff = (size_t)bh * (size_t)N * D;
-  const uint16_t* __restrict__ Qh = (const uint16_t*)p.q + hoff;
-  const uint16_t* __restrict__ Kh = (const uint16_t*)p.k + hoff;
-  const uint16_t* __restrict__ Vh = (const uint16_t*)p.v + hoff;
+  const uint16_t* Qh = (const uint16_t*)p.q + hoff;
+  const uint16_t* Kh = (const uint16_t*)p.k + hoff;
+  const uint16_t* Vh = (const uint16_t*)p.v + hoff;
 
   int n_vis = N;
   if (p.kv_lens) {
@@ -177,90 +200,101 @@ void fa_fwd_bf16_kernel(Params p) {
     n_vis = kl < 0 ? 0 : (kl > N ? N : kl);
   }
   const int q0 = qb * BM;
-  const int qw0 = q0 + wave * 32 * QW;
-  int kend = n_vis;
-  if (causal) kend = min(kend, q0 + BM);
-  const int nblk = (kend + kBN - 1) / kBN;
+  const int qw0 = q0 + wave * 32;
+  const int kend = causal ? min(n_vis, q0 + BM) : n_vis;
+  const int nblk = (kend + BN - 1) / BN;
 
-  // Q rows of this wave, in the B-operand layout of S^T = K Q^T.
-  u32x4_t qr[QW][KS];
+  // Q rows of this wave in the B-operand layout of S^T = K Q^T.  Rows past N
+  // lie outside the buffer range and read as zero.
+  u32x4_t qr[KS];
+  {
+    const rsrc_t rq = make_rsrc(Qh, (uint32_t)N * ROWB);
+    const uint32_t qoff = (uint32_t)(qw0 + n) * ROWB + 16u * hf;
 #pragma unroll
-  for (int qt = 0; qt < QW; ++qt) {
-    const int row = qw0 + 32 * qt + n;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4_t x = {0u, 0u, 0u, 0u};
-      if (row < N) x = *(const u32x4_t*)(Qh + (size_t)row * D + 16 * ks + 8 * hf);
-      qr[qt][ks] = x ^ p.qsign;
-    }
+    for (int ks = 0; ks < KS; ++ks) qr[ks] = buf_load16(rq, qoff + 32u * ks) ^ p.qsign;
   }
 
-  float m_run[QW], l_run[QW], le_run[QW];
-  f32x16_t acc[QW][DT];
+  // Global -> register staging of key block j.  K: row-major 16-byte
+  // pieces.  V: pieces of 4 keys x 8 dims, written to LDS transposed.  The
+  // buffer range of V ends at the last visible key, so hidden V rows arrive
+  // as zeros; K rows past N read zero.
+  uint32_t k_off[KU];
 #pragma unroll
-  for (int qt = 0; qt < QW; ++qt) {
-    m_run[qt] = -INFINITY;
-    l_run[qt] = 0.f;
-    le_run[qt] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[qt][dt][r] = 0.f;
+  for (int u = 0; u < KU; ++u) {
+    const int unit = tid + u * kThreads;
+    k_off[u] = (uint32_t)(unit / CPR) * ROWB + 16u * (unit % CPR);
   }
-
-  u32x4_t kreg[KU];
-  u32x4_t vreg[4];
-
-  // Global -> registers for key block j.  K pieces are row-major 16-byte
-  // chunks (coalesced).  V pieces are 4 keys x 8 dims so they can be written
-  // transposed with 8-byte LDS stores.  Keys >= N read nothing (zero); V rows
-  // of hidden padding keys are zeroed so that 0 * garbage cannot occur.
+  const bool v_unit = tid < VUNITS;
+  const int vkg = tid % (BN / 4), vdc = tid / (BN / 4);
+  const uint32_t v_off = (uint32_t)(4 * vkg) * ROWB + 16u * vdc;
+  u32x4_t kreg[KU], vreg[4];
   auto load_block = [&](int j) {
-    const int kbase = j * kBN;
-    const bool full = kbase + kBN <= n_vis;
+    const int kbase = j * BN;
+    const rsrc_t rk = make_rsrc(Kh + (size_t)kbase * D, (uint32_t)max(0, N - kbase) * ROWB);
+    const rsrc_t rv = make_rsrc(Vh + (size_t)kbase * D, (uint32_t)max(0, n_vis - kbase) * ROWB);
 #pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      const int unit = tid + u * kThreads;
-      const int key = unit / (D / 8);
-      const int ch = unit % (D / 8);
-      const int gk = kbase + key;
-      u32x4_t x = {0u, 0u, 0u, 0u};
-      if (full || gk < N) x = *(const u32x4_t*)(Kh + (size_t)gk * D + 8 * ch);
-      kreg[u] = x;
-    }
-    if (tid < VUNITS) {
-      const int kg = tid % (kBN / 4);
-      const int dc = tid / (kBN / 4);
+    for (int u = 0; u < KU; ++u) kreg[u] = buf_load16(rk, k_off[u]);
+    if (v_unit) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int gk = kbase + 4 * kg + i;
-        u32x4_t x = {0u, 0u, 0u, 0u};
-        if (full || gk < n_vis) x = *(const u32x4_t*)(Vh + (size_t)gk * D + 8 * dc);
-        vreg[i] = x;
-      }
+      for (int i = 0; i < 4; ++i) vreg[i] = buf_load16(rv, v_off + i * ROWB);
     }
   };
-
   auto store_block = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
       const int unit = tid + u * kThreads;
-      const int key = unit / (D / 8);
-      const int ch = unit % (D / 8);
-      *(u32x4_t*)&k_lds[buf][key][8 * ch] = kreg[u];
+      *(u32x4_t*)&k_lds[buf][unit / CPR][8 * (unit % CPR)] = kreg[u];
     }
-    if (tid < VUNITS) {
-      const int kg = tid % (kBN / 4);
-      const int dc = tid / (kBN / 4);
+    if (v_unit) {
+      // Dword w of key i holds dims 8*vdc + 2w, +1: regroup into
+      // (keys 0-3 of dim 2w) and (keys 0-3 of dim 2w+1).
 #pragma unroll
-      for (int pw = 0; pw < 4; ++pw) {
-        const unsigned a0 = vreg[0][pw], a1 = vreg[1][pw], a2 = vreg[2][pw], a3 = vreg[3][pw];
-        u32x2_t lo = {(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
-        u32x2_t hi = {(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
-        *(u32x2_t*)&vt_lds[buf][8 * dc + 2 * pw][4 * kg] = lo;
-        *(u32x2_t*)&vt_lds[buf][8 * dc + 2 * pw + 1][4 * kg] = hi;
+      for (int w = 0; w < 4; ++w) {
+        const unsigned a0 = vreg[0][w], a1 = vreg[1][w], a2 = vreg[2][w], a3 = vreg[3][w];
+        const u32x2_t lo = {__builtin_amdgcn_perm(a1, a0, 0x05040100u),
+                            __builtin_amdgcn_perm(a3, a2, 0x05040100u)};
+        const u32x2_t hi = {__builtin_amdgcn_perm(a1, a0, 0x07060302u),
+                            __builtin_amdgcn_perm(a3, a2, 0x07060302u)};
+        *(u32x2_t*)&vt_lds[buf][8 * vdc + 2 * w][4 * vkg] = lo;
+        *(u32x2_t*)&vt_lds[buf][8 * vdc + 2 * w + 1][4 * vkg] = hi;
       }
     }
+  };
+
+  float m_run = -INFINITY;   // reference max, log2 units (one query row per lane)
+  float l_run = 0.f;         // row sum of the bf16-rounded probabilities (normalises O)
+  float le_run = 0.f;        // row sum of the fp32 probabilities (gives LSE)
+  f32x16_t acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+  const float c = p.c;
+  const int krow = k_row_perm(n);
+  bool have_ref = false;   // wave-uniform: m_run was set by a full pass
+
+  // p = 2^(s*c - base), packed to bf16 as P^T (chunk pc = registers
+  // 8(pc%2)..+7 of key tile pc/2 = keys 16pc + 8hf + 0..7) with both row
+  // sums; the scores are left intact.
+  auto exps = [&](const f32x16_t (&s)[KT], u32x4_t (&pb)[PC], float base, float& re,
+                  float& rs) {
+    float re0 = 0.f, re1 = 0.f, rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+    for (int pc = 0; pc < PC; ++pc) {
+      const int kt = pc >> 1, r0 = 8 * (pc & 1);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r0 + 2 * w], c, -base));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r0 + 2 * w + 1], c, -base));
+        re0 += e0;
+        re1 += e1;
+        pb[pc][w] = pack_bf16(e0, e1);
+      }
+      rs0 = sum_bf16x2(pb[pc][0], sum_bf16x2(pb[pc][1], rs0));
+      rs1 = sum_bf16x2(pb[pc][2], sum_bf16x2(pb[pc][3], rs1));
+    }
+    re = re0 + re1;
+    rs = rs0 + rs1;
   };
 
   if (nblk > 0) {
@@ -269,140 +303,100 @@ void fa_fwd_bf16_kernel(Params p) {
   }
   __syncthreads();
 
-  const int krow = k_row_perm(n);
-  const float c = p.c;
-
   for (int j = 0; j < nblk; ++j) {
     const int buf = j & 1;
     const bool more = j + 1 < nblk;
     if (more) load_block(j + 1);
-    const int kbase = j * kBN;
-    const bool wave_skip = causal && (kbase > qw0 + 32 * QW - 1);
+    const int kbase = j * BN;
+    const bool wave_skip = causal && (kbase > qw0 + 31);
     if (!wave_skip) {
-      // S^T = K_j Q^T
-      f32x16_t s[QW][KT];
+      // S^T = K_j Q^T with K rows permuted (row 32kt + krow feeds MFMA row n).
+      f32x16_t s[KT];
 #pragma unroll
-      for (int qt = 0; qt < QW; ++qt)
+      for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
+        for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[qt][kt][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+      for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt) {
           const u32x4_t a = *(const u32x4_t*)&k_lds[buf][32 * kt + krow][16 * ks + 8 * hf];
-#pragma unroll
-          for (int qt = 0; qt < QW; ++qt) s[qt][kt] = mfma_bf16(a, qr[qt][ks], s[qt][kt]);
+          s[kt] = mfma_bf16(a, qr[ks], s[kt]);
         }
-      }
-
-      const bool need_mask = (causal && kbase + kBN - 1 > qw0) || (kbase + kBN > n_vis);
-      if (need_mask) {
-#pragma unroll
-        for (int qt = 0; qt < QW; ++qt) {
-          const int qrow = qw0 + 32 * qt + n;
-#pragma unroll
-          for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = kbase + 32 * kt + 16 * (r >> 3) + 8 * hf + (r & 7);
-              const bool hide = (causal && key > qrow) || key >= n_vis;
-              if (hide) s[qt][kt][r] = -INFINITY;
-            }
-        }
-      }
-
-      u32x4_t pb[QW][PC];
-#pragma unroll
-      for (int qt = 0; qt < QW; ++qt) {
-        float mx = s[qt][0][0];
+      // Register r of key tile kt holds key kbase + 32kt + 16(r/8) + 8hf + r%8.
+      if ((causal && kbase + BN - 1 > qw0) || kbase + BN > n_vis) {
+        const int qrow = qw0 + n;
+        const int lim = (causal ? min(qrow, n_vis - 1) : n_vis - 1) - kbase - 8 * hf;
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qt][kt][r]);
-        mx = pair_max(mx);
-        const float mt = mx * c;                  // block max, log2 units
-        const bool upd = mt > m_run[qt] + kTau;   // false while nothing is visible
-        float alpha = 1.f;
-        if (__any(upd)) {
-          const float m_new = upd ? mt : m_run[qt];
-          alpha = upd ? __builtin_amdgcn_exp2f(m_run[qt] - m_new) : 1.f;
-          m_run[qt] = m_new;
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[qt][dt][r] *= alpha;
-        }
-        const float base = (m_run[qt] == -INFINITY) ? 0.f : m_run[qt];
-        float re0 = 0.f, re1 = 0.f;
+          for (int r = 0; r < 16; ++r)
+            if (32 * kt + 16 * (r >> 3) + (r & 7) > lim) s[kt][r] = -INFINITY;
+      }
+
+      // Exponentials against the reference max.  A wave's first block, or a
+      // block whose fp32 row sum shows a probability above 2^20 (or an
+      // infinite one), takes the full path: block row max, move the
+      // reference, rescale the state, redo the exponentials.
+      u32x4_t pb[PC];
+      float re = 0.f, rs = 0.f;
+      bool full = !have_ref;
+      if (!full) {
+        exps(s, pb, m_run, re, rs);
+        full = __any(!(re <= kOverflowSum));
+      }
+      if (full) {
+        float mx = s[0][0];
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-          for (int r = 0; r < 16; r += 2) {
-            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qt][kt][r], c, -base));
-            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qt][kt][r + 1], c, -base));
-            s[qt][kt][r] = e0;
-            s[qt][kt][r + 1] = e1;
-            re0 += e0;
-            re1 += e1;
-          }
-        // Two row sums: the fp32 one gives LSE; the one over the
-        // bf16-rounded probabilities (the weights that actually multiply V)
-        // normalises O, so those weights sum to exactly 1.
-        float rs0 = 0.f, rs1 = 0.f;
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+        const float m_new = fmaxf(m_run, pair_max(mx) * c);
+        const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
-        for (int pc = 0; pc < PC; ++pc) {
-          const int kt = pc >> 1, r0 = 8 * (pc & 1);
-          u32x4_t x;
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-          for (int w = 0; w < 4; ++w)
-            x[w] = pack_bf16(s[qt][kt][r0 + 2 * w], s[qt][kt][r0 + 2 * w + 1]);
-          pb[qt][pc] = x;
-          rs0 = sum_bf16x2(x[0], sum_bf16x2(x[1], rs0));
-          rs1 = sum_bf16x2(x[2], sum_bf16x2(x[3], rs1));
-        }
-        l_run[qt] = l_run[qt] * alpha + (rs0 + rs1);
-        le_run[qt] = le_run[qt] * alpha + (re0 + re1);
+          for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+        l_run *= alpha;
+        le_run *= alpha;
+        m_run = m_new;
+        have_ref = true;
+        exps(s, pb, (m_new == -INFINITY) ? 0.f : m_new, re, rs);
       }
+      l_run += rs;
+      le_run += re;
 
-      // O^T += V_j^T P^T
+      // O^T += V_j^T P^T: A operand = V^T rows 32dt + n, keys 16pc + 8hf + 0..7.
 #pragma unroll
-      for (int pc = 0; pc < PC; ++pc) {
+      for (int pc = 0; pc < PC; ++pc)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
           const u32x4_t a = *(const u32x4_t*)&vt_lds[buf][32 * dt + n][16 * pc + 8 * hf];
-#pragma unroll
-          for (int qt = 0; qt < QW; ++qt) acc[qt][dt] = mfma_bf16(a, pb[qt][pc], acc[qt][dt]);
+          acc[dt] = mfma_bf16(a, pb[pc], acc[dt]);
         }
-      }
     }
-    if (more) store_block((j + 1) & 1);
+    if (more) store_block(buf ^ 1);
     __syncthreads();
   }
 
-  // Epilogue: O = acc / l (rounded to bf16 once), LSE = (m + log2 l) * ln 2.
+  // Epilogue: O = acc / l (rounded to bf16 once), LSE = (m + log2 le) * ln 2.
   uint16_t* __restrict__ Oh = (uint16_t*)p.o + hoff;
   float* __restrict__ Lh = p.lse + (size_t)bh * N;
+  const float lt = pair_sum(l_run);
+  const float le = pair_sum(le_run);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const int qrow = qw0 + n;
+  if (qrow < N) {
+    uint16_t* orow = Oh + (size_t)qrow * D;
 #pragma unroll
-  for (int qt = 0; qt < QW; ++qt) {
-    const float lt = pair_sum(l_run[qt]);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const int qrow = qw0 + 32 * qt + n;
-    if (qrow < N) {
-      uint16_t* orow = Oh + (size_t)qrow * D;
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          u32x2_t x = {pack_bf16(acc[qt][dt][4 * a] * inv, acc[qt][dt][4 * a + 1] * inv),
-                       pack_bf16(acc[qt][dt][4 * a + 2] * inv, acc[qt][dt][4 * a + 3] * inv)};
-          *(u32x2_t*)(orow + 32 * dt + 8 * a + 4 * hf) = x;
-        }
-      const float le = pair_sum(le_run[qt]);
-      if (hf == 0)
-        Lh[qrow] = lt > 0.f ? (m_run[qt] + __builtin_amdgcn_logf(le)) * kLn2 : -INFINITY;
-    }
+      for (int a = 0; a < 4; ++a) {
+        u32x2_t x = {pack_bf16(acc[dt][4 * a] * inv, acc[dt][4 * a + 1] * inv),
+                     pack_bf16(acc[dt][4 * a + 2] * inv, acc[dt][4 * a + 3] * inv)};
+        *(u32x2_t*)(orow + 32 * dt + 8 * a + 4 * hf) = x;
+      }
+    if (hf == 0) Lh[qrow] = lt > 0.f ? (m_run + __builtin_amdgcn_logf(le)) * kLn2 : -INFINITY;
   }
 }
 
@@ -551,10 +545,6 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(Params p) {
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
-#ifndef FA_QW
-#define FA_QW 1
-#endif
-constexpr int kQW = FA_QW;  // 32-query tiles per wave in the bf16 kernel
 
 int check_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
                int B, int H, int N, int d, float scale, int mask_kind, const int32_t* kv_lens,
@@ -569,6 +559,9 @@ int check_args(const void* q, const void* k, const void* v, const void* o, const
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   const long long nqb = ((long long)N + bm - 1) / bm;
   if ((long long)B * H * nqb > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  // One head's rows (plus one block of rows past the end) are addressed with
+  // 32-bit byte offsets.
+  if (((long long)N + bm) * d * 4 > 0xffffffffLL) return FA_ERR_INVALID_ARG;
   return FA_OK;
 }
 
@@ -597,7 +590,7 @@ Params make_params(const void* q, const void* k, const void* v, void* o, float* 
 extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                       int H, int N, int d, float scale, int mask_kind, const int32_t* kv_lens,
                       void* stream) {
-  constexpr int BM = 32 * kQW * kWaves;
+  constexpr int BM = 32 * kWaves;
   const int st = check_args(q, k, v, o, lse, B, H, N, d, scale, mask_kind, kv_lens, BM);
   if (st != FA_OK) return st;
   const int nqb = (N + BM - 1) / BM;
@@ -605,9 +598,9 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
   const dim3 grid((unsigned)(B * H * nqb)), block(kThreads);
   hipStream_t s = (hipStream_t)stream;
   if (d == 128)
-    hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, kQW>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fa_fwd_bf16_kernel<128>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, kQW>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fa_fwd_bf16_kernel<64>), grid, block, 0, s, p);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
