@@ -14,12 +14,14 @@
 // Mapping to CDNA4 (the design notes of the repository give the measurements
 // behind each choice):
 //
-//  * One workgroup = 4 wavefronts = one block of 128 query rows of one
+//  * One workgroup = 8 wavefronts = one block of 256 query rows of one
 //    (batch, head); each wave owns 32 rows, the N dimension of a 32x32 MFMA
-//    tile.  Two workgroups share a CU (2 waves per SIMD), so one wave's
-//    MFMAs overlap the other's softmax.  Blocks of 64 keys are staged through
-//    LDS, double buffered: raw buffer loads bring block j+1 into registers
-//    while block j is computed (rows past the end read as zero).
+//    tile.  Two waves share each SIMD, so one wave's MFMAs overlap the
+//    other's softmax.  Blocks of 64 keys are staged through LDS, double
+//    buffered: raw buffer loads bring block j+1 into registers while block j
+//    is computed (rows past the end read as zero).  LDS operand reads are
+//    issued well ahead of their MFMAs (scheduling hints), since an LDS round
+//    trip under load spans about ten MFMA issue intervals.
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: the accumulator holds ONE query row per lane
 //    (lane % 32) and 16 keys per lane, so the softmax row statistics are
@@ -124,6 +126,22 @@ __device__ __forceinline__ int k_row_perm(int m) {
   return (m & 0x13) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
+// Scheduling hint for a run of NM MFMAs, each fed by one LDS operand read:
+// issue AHEAD reads first, then alternate MFMA and read.  LDS round trips
+// under load are ~10 MFMA issue intervals, so the reads must run well ahead.
+#ifndef FA_READ_AHEAD
+#define FA_READ_AHEAD 6
+#endif
+template <int NM, int AHEAD>
+__device__ __forceinline__ void mfma_read_ahead() {
+  if (AHEAD > 0) __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i + AHEAD < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+}
+
 // Maps the linear workgroup id to (head, query block).  Workgroups are
 // dispatched round-robin over 8 XCDs; when the grid divides evenly, XCD x
 // gets the contiguous logical range [x*G/8, (x+1)*G/8).  Within a head,
@@ -156,13 +174,23 @@ struct Params {
 #ifndef FA_WAVES_PER_EU
 #define FA_WAVES_PER_EU 2
 #endif
+#ifndef FA_V_PREFETCH
+#define FA_V_PREFETCH 8
+#endif
 
+
+#ifndef FA_BF16_WAVES
+#define FA_BF16_WAVES 8
+#endif
+constexpr int kBWaves = FA_BF16_WAVES;     // waves per workgroup, bf16 kernel
+constexpr int kBThreads = 64 * kBWaves;
 
 template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FA_WAVES_PER_EU)))
+__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(FA_WAVES_PER_EU)))
 void fa_fwd_bf16_kernel(Params p) {
+  constexpr int kThreads = kBThreads;
   constexpr int BN = 64;            // keys per block
-  constexpr int BM = 32 * kWaves;   // query rows per workgroup
+  constexpr int BM = 32 * kBWaves;  // query rows per workgroup
   constexpr int KS = D / 16;        // MFMA k-steps over d for S^T
   constexpr int DT = D / 32;        // 32-row tiles of O^T
   constexpr int KT = BN / 32;       // 32-key tiles of S^T
@@ -224,7 +252,7 @@ void fa_fwd_bf16_kernel(Params p) {
     const int unit = tid + u * kThreads;
     k_off[u] = (uint32_t)(unit / CPR) * ROWB + 16u * (unit % CPR);
   }
-  const bool v_unit = tid < VUNITS;
+  const bool v_unit = tid < VUNITS;   // VUNITS <= kThreads: one piece per thread at most
   const int vkg = tid % (BN / 4), vdc = tid / (BN / 4);
   const uint32_t v_off = (uint32_t)(4 * vkg) * ROWB + 16u * vdc;
   u32x4_t kreg[KU], vreg[4];
@@ -323,6 +351,14 @@ void fa_fwd_bf16_kernel(Params p) {
           const u32x4_t a = *(const u32x4_t*)&k_lds[buf][32 * kt + krow][16 * ks + 8 * hf];
           s[kt] = mfma_bf16(a, qr[ks], s[kt]);
         }
+      mfma_read_ahead<KS * KT, FA_READ_AHEAD>();
+      // The first V^T operands are requested now, so they arrive while the
+      // softmax runs.
+      constexpr int VPRE = FA_V_PREFETCH;
+      u32x4_t vpre[VPRE > 0 ? VPRE : 1];
+#pragma unroll
+      for (int i = 0; i < VPRE; ++i)
+        vpre[i] = *(const u32x4_t*)&vt_lds[buf][32 * (i % DT) + n][16 * (i / DT) + 8 * hf];
       // Register r of key tile kt holds key kbase + 32kt + 16(r/8) + 8hf + r%8.
       if ((causal && kbase + BN - 1 > qw0) || kbase + BN > n_vis) {
         const int qrow = qw0 + n;
@@ -371,9 +407,12 @@ void fa_fwd_bf16_kernel(Params p) {
       for (int pc = 0; pc < PC; ++pc)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const u32x4_t a = *(const u32x4_t*)&vt_lds[buf][32 * dt + n][16 * pc + 8 * hf];
+          const int i = pc * DT + dt;
+          const u32x4_t a = i < VPRE ? vpre[i < VPRE ? i : 0]
+                                     : *(const u32x4_t*)&vt_lds[buf][32 * dt + n][16 * pc + 8 * hf];
           acc[dt] = mfma_bf16(a, pb[pc], acc[dt]);
         }
+      mfma_read_ahead<PC * DT, (PC * DT - VPRE < FA_READ_AHEAD ? PC * DT - VPRE : FA_READ_AHEAD)>();
     }
     if (more) store_block(buf ^ 1);
     __syncthreads();
@@ -590,12 +629,12 @@ Params make_params(const void* q, const void* k, const void* v, void* o, float* 
 extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                       int H, int N, int d, float scale, int mask_kind, const int32_t* kv_lens,
                       void* stream) {
-  constexpr int BM = 32 * kWaves;
+  constexpr int BM = 32 * kBWaves;
   const int st = check_args(q, k, v, o, lse, B, H, N, d, scale, mask_kind, kv_lens, BM);
   if (st != FA_OK) return st;
   const int nqb = (N + BM - 1) / BM;
   const Params p = make_params(q, k, v, o, lse, H, N, nqb, scale, mask_kind, kv_lens);
-  const dim3 grid((unsigned)(B * H * nqb)), block(kThreads);
+  const dim3 grid((unsigned)(B * H * nqb)), block(kBThreads);
   hipStream_t s = (hipStream_t)stream;
   if (d == 128)
     hipLaunchKernelGGL((fa_fwd_bf16_kernel<128>), grid, block, 0, s, p);
