@@ -143,12 +143,25 @@ __device__ __forceinline__ void mfma_read_ahead() {
 }
 
 // Maps the linear workgroup id to (head, query block).  Workgroups are
-// dispatched round-robin over 8 XCDs; when the grid divides evenly, XCD x
-// gets the contiguous logical range [x*G/8, (x+1)*G/8).  Within a head,
-// causal query blocks are visited from the last (heaviest) to the first.
+// dispatched round-robin over the 8 XCDs (w % 8), and in order within one.
+// When the heads split evenly, XCD x owns a contiguous range of heads (their
+// K/V share its L2) and visits their query blocks rank by rank: for causal
+// masks the last (heaviest) query block of every head first, so the light
+// ones fill the tail.  Otherwise XCD x gets the contiguous logical range
+// [x*G/8, (x+1)*G/8), heavy query blocks first within each head.
 __device__ __forceinline__ void map_block(int nqb, bool causal, int& bh, int& qb) {
   const int G = gridDim.x;
   const int w = blockIdx.x;
+  const int BH = G / nqb;
+  if (G % 8 == 0 && BH % 8 == 0) {
+    // XCD x = w % 8 owns heads [x*BH/8, (x+1)*BH/8); it visits their query
+    // blocks rank by rank (heaviest causal rank first), head by head.
+    const int hx = BH / 8, i = w / 8;
+    bh = (w % 8) * hx + i % hx;
+    const int r = i / hx;
+    qb = causal ? (nqb - 1 - r) : r;
+    return;
+  }
   const int L = (G % 8 == 0) ? (w % 8) * (G / 8) + w / 8 : w;
   bh = L / nqb;
   const int r = L - bh * nqb;
@@ -179,18 +192,12 @@ struct Params {
 #endif
 
 
-#ifndef FA_BF16_WAVES
-#define FA_BF16_WAVES 8
-#endif
-constexpr int kBWaves = FA_BF16_WAVES;     // waves per workgroup, bf16 kernel
-constexpr int kBThreads = 64 * kBWaves;
-
-template <int D>
-__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(FA_WAVES_PER_EU)))
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(FA_WAVES_PER_EU)))
 void fa_fwd_bf16_kernel(Params p) {
-  constexpr int kThreads = kBThreads;
+  constexpr int kThreads = 64 * NW;
   constexpr int BN = 64;            // keys per block
-  constexpr int BM = 32 * kBWaves;  // query rows per workgroup
+  constexpr int BM = 32 * NW;       // query rows per workgroup
   constexpr int KS = D / 16;        // MFMA k-steps over d for S^T
   constexpr int DT = D / 32;        // 32-row tiles of O^T
   constexpr int KT = BN / 32;       // 32-key tiles of S^T
@@ -624,22 +631,33 @@ Params make_params(const void* q, const void* k, const void* v, void* o, float* 
   return p;
 }
 
+constexpr long long kCUs = 256;   // compute units of an MI355X
+
 }  // namespace
 
 extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                       int H, int N, int d, float scale, int mask_kind, const int32_t* kv_lens,
                       void* stream) {
-  constexpr int BM = 32 * kBWaves;
-  const int st = check_args(q, k, v, o, lse, B, H, N, d, scale, mask_kind, kv_lens, BM);
+  const int st = check_args(q, k, v, o, lse, B, H, N, d, scale, mask_kind, kv_lens, 256);
   if (st != FA_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  // 256-row workgroups (8 waves, one per CU) share each K/V tile among more
+  // rows.  They are used when they fill the 256 CUs at least once (twice for
+  // causal masks, whose query blocks differ in cost); otherwise 128-row
+  // workgroups (two per CU) balance better.
+  const long long grid256 = (long long)B * H * ((N + 255) / 256);
+  const bool big = grid256 >= ((mask_kind & FA_MASK_CAUSAL) ? 2 : 1) * kCUs;
+  const int BM = big ? 256 : 128;
   const int nqb = (N + BM - 1) / BM;
   const Params p = make_params(q, k, v, o, lse, H, N, nqb, scale, mask_kind, kv_lens);
-  const dim3 grid((unsigned)(B * H * nqb)), block(kBThreads);
-  hipStream_t s = (hipStream_t)stream;
-  if (d == 128)
-    hipLaunchKernelGGL((fa_fwd_bf16_kernel<128>), grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL((fa_fwd_bf16_kernel<64>), grid, block, 0, s, p);
+  const dim3 grid((unsigned)(B * H * nqb)), block(big ? 512 : 256);
+  if (d == 128) {
+    if (big) hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, 8>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, 4>), grid, block, 0, s, p);
+  } else {
+    if (big) hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, 8>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, 4>), grid, block, 0, s, p);
+  }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
