@@ -142,6 +142,9 @@ __device__ __forceinline__ void mfma_read_ahead() {
   }
 }
 
+#ifndef FA_HEAD_GROUP
+#define FA_HEAD_GROUP 2
+#endif
 // Maps the linear workgroup id to (head, query block).  Workgroups are
 // dispatched round-robin over the 8 XCDs (w % 8), and in order within one.
 // When the heads split evenly, XCD x owns a contiguous range of heads (their
@@ -157,8 +160,10 @@ __device__ __forceinline__ void map_block(int nqb, bool causal, int& bh, int& qb
     // XCD x = w % 8 owns heads [x*BH/8, (x+1)*BH/8); it visits their query
     // blocks rank by rank (heaviest causal rank first), head by head.
     const int hx = BH / 8, i = w / 8;
-    bh = (w % 8) * hx + i % hx;
-    const int r = i / hx;
+    const int g = (hx % FA_HEAD_GROUP == 0) ? FA_HEAD_GROUP : hx;   // heads visited together
+    const int grp = i / (g * nqb), j = i - grp * (g * nqb);
+    bh = (w % 8) * hx + grp * g + j % g;
+    const int r = j / g;
     qb = causal ? (nqb - 1 - r) : r;
     return;
   }
