@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the attention forward pass.
+"""Seeded synthetic inputs for the attention forward and backward passes.
 
 This module only draws and encodes numbers: it holds none of the attention
 arithmetic.  Both the CPU oracle's tests and the GPU path's tests and bench
@@ -15,6 +15,10 @@ Recipe (identical for every workload):
   round-to-nearest-even and keep them as uint16 bit patterns.
 * Key-padding workloads draw one valid key length per batch entry,
   uniform over the inclusive integer range ``kv_len_range``.
+* The backward pass's upstream gradient dO (same shape as O) comes from a
+  fifth stream, ``SeedSequence(seed).spawn(5)[4]`` (the first four children
+  are the ones above, so the forward inputs do not change): float32
+  ``standard_normal``, then bf16 as above for bf16 workloads.
 """
 from __future__ import annotations
 
@@ -53,6 +57,11 @@ class Workload:
         """Forward FLOPs by the metric's formula: 4*B*H*N^2*d, halved when causal."""
         f = 4.0 * self.B * self.H * self.N * self.N * self.d
         return f / 2.0 if (self.mask_kind & MASK_CAUSAL) else f
+
+    def bwd_flops(self) -> float:
+        """Backward FLOPs by the same convention: the five products of the
+        gradient (S, dP, dV, dQ, dK; 2*N^2*d each), i.e. 2.5x the forward."""
+        return 2.5 * self.flops()
 
 
 # The five workloads the parity tests and the bench use.  Seeds are fixed per
@@ -104,9 +113,9 @@ def bf16_bits_to_f32(u: np.ndarray) -> np.ndarray:
     return (u.astype(np.uint32) << 16).view(np.float32)
 
 
-def _streams(seed: int):
+def _streams(seed: int, n: int = 4):
     return [np.random.Generator(np.random.PCG64(s))
-            for s in np.random.SeedSequence(seed).spawn(4)]
+            for s in np.random.SeedSequence(seed).spawn(n)]
 
 
 def make_raw(B: int, H: int, N: int, d: int, dtype: str, seed: int,
@@ -135,10 +144,26 @@ def make_raw(B: int, H: int, N: int, d: int, dtype: str, seed: int,
     return {"q": q, "k": k, "v": v, "kv_lens": kv_lens}
 
 
+def make_grad_out(B: int, H: int, N: int, d: int, dtype: str, seed: int):
+    """Draw the upstream gradient dO ``[B, H, N, d]`` for the backward pass."""
+    if dtype not in ("f32", "bf16"):
+        raise ValueError(f"dtype must be 'f32' or 'bf16', got {dtype!r}")
+    g = _streams(seed, 5)[4]
+    do = g.standard_normal((B, H, N, d), dtype=np.float32)
+    return f32_to_bf16_bits(do) if dtype == "bf16" else do
+
+
 def make_inputs(wl: Workload):
     """Draw the inputs of a named workload (see ``WORKLOADS``)."""
     return make_raw(wl.B, wl.H, wl.N, wl.d, wl.dtype, wl.seed,
                     q_mult=wl.q_mult, kv_len_range=wl.kv_len_range)
+
+
+def make_bwd_inputs(wl: Workload):
+    """The forward inputs of a workload plus its upstream gradient ``do``."""
+    x = make_inputs(wl)
+    x["do"] = make_grad_out(wl.B, wl.H, wl.N, wl.d, wl.dtype, wl.seed)
+    return x
 
 
 def to_f64(x: np.ndarray) -> np.ndarray:

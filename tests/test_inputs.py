@@ -56,3 +56,18 @@ def test_flop_formula():
     assert wl.flops() == 4 * 2 * 32 * 4096 * 4096 * 128 / 2
     assert abs(wl.scale - 1 / np.sqrt(128)) < 1e-8
     assert to_f64(np.array([0x3F80], np.uint16))[0] == 1.0
+
+
+def test_grad_out_stream_leaves_forward_inputs_unchanged():
+    """dO comes from a fifth child seed; Q, K, V keep their streams."""
+    from fa_inputs import make_bwd_inputs, make_grad_out
+    wl = WORKLOADS["bf16_b4h16_n1024_d64_causal"]
+    x = make_inputs(wl)
+    y = make_bwd_inputs(wl)
+    for n in "qkv":
+        assert np.array_equal(x[n], y[n])
+    assert y["do"].shape == x["q"].shape and y["do"].dtype == np.uint16
+    assert np.array_equal(y["do"], make_grad_out(wl.B, wl.H, wl.N, wl.d, "bf16", wl.seed))
+    assert not np.array_equal(y["do"], y["q"])
+    f = make_grad_out(1, 2, 8, 4, "f32", 3)
+    assert f.dtype == np.float32 and abs(float(f.mean())) < 1.0
