@@ -1,7 +1,7 @@
-"""Exact attention forward on MI355X (gfx950): Python binding of libfa92.so.
+"""Exact attention on MI355X (gfx950): Python binding of libfa92.so.
 
-The binding only marshals arguments: every step of the forward pass runs in
-the HIP kernels of ``csrc/fa_fwd.hip``.  PyTorch supplies device memory and
+The binding only marshals arguments: every step of the forward and backward
+passes runs in the HIP kernels of ``csrc/fa_fwd.hip`` and ``csrc/fa_bwd.hip``.  PyTorch supplies device memory and
 the stream.  There is no CPU or PyTorch fallback: if the library is missing
 or the GPU is absent, the calls raise.
 
@@ -10,6 +10,8 @@ Names follow the C ABI of ``include/fa_api.h``:
 * ``fa_fwd(q, k, v, o, lse, scale, mask_kind=0, kv_lens=None, stream=None)``
   -- bf16 tensors ``[B, H, N, d]``
 * ``fa_fwd_f32(...)`` -- the same with float32 tensors
+* ``fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, dp_rowsum, scale, mask_kind=0,
+  kv_lens=None, stream=None)`` -- bf16 gradients
 * ``fa_strerror(status)``
 
 ``attention(q, k, v, ...)`` allocates ``o`` and ``lse`` and calls the right
@@ -30,7 +32,7 @@ FA_ERR_UNSUPPORTED = -2
 FA_ERR_HIP = -3
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa92.so")
-EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_strerror")
+EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_strerror")
 
 _lib = None
 
@@ -56,6 +58,8 @@ def load_library():
         fn = getattr(lib, name)
         fn.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, vp]
         fn.restype = i32
+    lib.fa_bwd.argtypes = [vp] * 10 + [i32, i32, i32, i32, f32, i32, vp, vp]
+    lib.fa_bwd.restype = i32
     lib.fa_strerror.argtypes = [i32]
     lib.fa_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -108,6 +112,55 @@ def fa_fwd_f32(q, k, v, o, lse, scale, mask_kind=FA_MASK_NONE, kv_lens=None, str
     """float32 forward: writes o (float32) and lse (float32) on ``stream``."""
     import torch
     _call("fa_fwd_f32", q, k, v, o, lse, scale, mask_kind, kv_lens, stream, torch.float32)
+
+
+def _stream_handle(stream, device):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, dp_rowsum, scale, mask_kind=FA_MASK_NONE,
+           kv_lens=None, stream=None):
+    """bf16 backward: writes dq, dk, dv (bf16) and dp_rowsum (float32 [B, H, N])."""
+    import torch
+    lib = load_library()
+    for nm, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq),
+                  ("dk", dk), ("dv", dv)):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{nm} must be torch.bfloat16, got {t.dtype}")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{nm} must be a contiguous device tensor")
+        if t.dim() != 4 or t.shape != q.shape:
+            raise ValueError(f"{nm} must have the shape of q, [B, H, N, d]")
+    B, H, N, d = q.shape
+    for nm, t in (("lse", lse), ("dp_rowsum", dp_rowsum)):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() \
+                or tuple(t.shape) != (B, H, N):
+            raise ValueError(f"{nm} must be a contiguous float32 device tensor [B, H, N]")
+    if kv_lens is not None:
+        if kv_lens.dtype != torch.int32 or not kv_lens.is_cuda or kv_lens.numel() != B:
+            raise ValueError("kv_lens must be an int32 device tensor [B]")
+    st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                    _ptr(dk), _ptr(dv), _ptr(dp_rowsum), B, H, N, d, float(scale),
+                    int(mask_kind), _ptr(kv_lens),
+                    ctypes.c_void_p(_stream_handle(stream, q.device)))
+    if st != FA_OK:
+        raise FaError(st, fa_strerror(st))
+
+
+def attention_grad(q, k, v, o, lse, dout, scale=None, mask_kind=FA_MASK_NONE, kv_lens=None,
+                   stream=None):
+    """Allocate the gradients and run the backward pass; returns ``(dq, dk, dv)``."""
+    import torch
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = d ** -0.5
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dps = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, dps, scale, mask_kind, kv_lens, stream)
+    return dq, dk, dv
 
 
 def attention(q, k, v, scale=None, mask_kind=FA_MASK_NONE, kv_lens=None, stream=None):

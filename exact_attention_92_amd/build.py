@@ -11,7 +11,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "fa_fwd.hip")
+SRCS = [os.path.join(PKG, "csrc", f) for f in ("fa_fwd.hip", "fa_bwd.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa92.so")
 ARCH = "gfx950"
@@ -34,7 +34,7 @@ def hipcc() -> str:
 def build(verbose: bool = False) -> str:
     """Compile libfa92.so (always recompiles) and return its path."""
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", SRC, "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, f"-I{INCLUDE}", *SRCS, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

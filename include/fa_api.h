@@ -1,5 +1,6 @@
 /*
- * fa_api.h -- C ABI of the exact attention forward library (libfa92.so).
+ * fa_api.h -- C ABI of the exact attention library (libfa92.so): the
+ * forward pass and the backward pass.
  *
  * What the library computes, for every batch entry b and head h:
  *
@@ -89,6 +90,39 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int N, int d, float scale, int mask_kind,
                const int32_t* kv_lens, void* stream);
+
+/* bfloat16 backward: the gradients of the attention above with respect to
+ * q, k and v, given the upstream gradient dout = dL/dO.  With P the softmax
+ * probabilities of the forward ("FlashAttention算法详解：从IO瓶颈到Triton实现",
+ * section Backward为什么更复杂, with the scale carried by the scores):
+ *
+ *     dv = P^T dout
+ *     dP = dout v^T,   dS = P * (dP - rowsum(dP * P))   (elementwise)
+ *     dq = scale * dS k,   dk = scale * dS^T q
+ *
+ * P is rebuilt block by block from q, k and the forward's lse, so o and lse
+ * must be the outputs of fa_fwd on the same q, k, v, scale, mask_kind and
+ * kv_lens.  rowsum(dP * P) is computed as rowsum(dout * o), which is equal
+ * since O = P V.
+ *
+ *  - q, k, v, o, dout: DEVICE pointers, bf16 [B, H, N, d], read only.
+ *  - lse: DEVICE pointer, float32 [B, H, N], read only.
+ *  - dq, dk, dv: DEVICE pointers, bf16 [B, H, N, d], written (every element;
+ *    keys that no query sees get dk = dv = 0, a query that sees no key gets
+ *    dq = 0).  Rounded to bf16 once, at the end.
+ *  - dp_rowsum: DEVICE pointer, float32 [B, H, N], written with
+ *    rowsum(dP * P) of every query row; the call also reads it back, so it
+ *    is caller-owned scratch that must not alias any other argument.
+ *  - Output buffers must not overlap each other or the inputs.
+ *  - Sizes, scale, mask_kind, kv_lens, alignment, stream and errors: as for
+ *    fa_fwd.  The call enqueues two kernels on the stream (dq and
+ *    dp_rowsum, then dk and dv) and returns without synchronising; it
+ *    allocates nothing and uses no atomics, so results are bitwise
+ *    reproducible. */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+           float* dp_rowsum, int B, int H, int N, int d, float scale,
+           int mask_kind, const int32_t* kv_lens, void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* fa_strerror(int status);

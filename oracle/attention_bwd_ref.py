@@ -73,15 +73,24 @@ def _visible(rows, cols, causal, n_vis):
     return np.broadcast_to(vis, (len(rows), len(cols)))
 
 
-def _head_bwd(qh, kh, vh, doh, scale, causal, n_vis, row_block):
-    """dQ, dK, dV and rowsum(dP * P) of one (b, h), by the definition."""
+def _head_bwd(qh, kh, vh, doh, scale, causal, n_vis, rows, row_block, mags):
+    """dQ, dK, dV and rowsum(dP * P) of one (b, h), by the definition, with
+    the contributions of the query rows ``rows`` (sorted).  When ``mags`` is
+    a dict, it also receives the magnitudes described in attention_bwd_ref."""
     N, d = qh.shape
-    dq = np.zeros((N, d))
+    dq = np.full((N, d), np.nan)
     dk = np.zeros((N, d))
     dv = np.zeros((N, d))
-    dps = np.zeros(N)
-    for start in range(0, N, row_block):
-        rr = np.arange(start, min(N, start + row_block))
+    dps = np.full(N, np.nan)
+    dq[rows] = 0.0
+    dps[rows] = 0.0
+    if mags is not None:
+        mags.update(dq=np.full((N, d), np.nan), dk=np.zeros((N, d)), dv=np.zeros((N, d)),
+                    dps=np.full(N, np.nan))
+        mags["dq"][rows] = 0.0
+        mags["dps"][rows] = 0.0
+    for start in range(0, len(rows), row_block):
+        rr = rows[start:start + row_block]
         kmax = min(n_vis, int(rr[-1]) + 1) if causal else n_vis
         if kmax <= 0:
             continue
@@ -100,6 +109,14 @@ def _head_bwd(qh, kh, vh, doh, scale, causal, n_vis, row_block):
         dq[rr] = (ds @ kh[:kmax]) * scale         # dQ = scale dS K
         dk[:kmax] += (ds.T @ qh[rr]) * scale      # dK = scale dS^T Q
         dps[rr] = rs
+        if mags is not None:
+            aq, ak, av, ado = (np.abs(t) for t in (qh[rr], kh[:kmax], vh[:kmax], doh[rr]))
+            ads = np.abs(ds)
+            a_d = (ado * (p @ av)).sum(axis=1)            # sum_t |dO| (P |V|)
+            mags["dps"][rr] = a_d
+            mags["dv"][:kmax] += p.T @ ado
+            mags["dq"][rr] = scale * (ads @ ak + a_d[:, None] * (p @ ak))
+            mags["dk"][:kmax] += scale * (ads.T @ aq + p.T @ (a_d[:, None] * aq))
     return dq, dk, dv, dps
 
 
@@ -121,27 +138,52 @@ def _n_vis(mask_kind, kv_lens, b, N):
 
 
 def attention_bwd_ref(q, k, v, do, scale, mask_kind=0, kv_lens=None, heads=None,
-                      row_block: int = 512, workers: int = 1):
+                      rows=None, row_block: int = 512, workers: int = 1,
+                      magnitudes: bool = False):
     """fp64 gradients of exact attention.
 
     q, k, v, do: float64 ``[B, H, N, d]``.  ``heads``: optional list of
-    (b, h) pairs to compute (default all; the others stay NaN).  Returns
+    (b, h) pairs to compute (default all; the others stay NaN).  ``rows``:
+    optional sorted query-row indices; only those rows' terms are summed, so
+    dQ and dp_rowsum are exact on them (NaN elsewhere) and dK, dV are exact
+    for every key that no other row sees (under the causal mask: every key
+    at or after the first row of a contiguous tail ``rows``).  Returns
     ``dQ, dK, dV`` (``[B, H, N, d]``) and ``dp_rowsum`` (``[B, H, N]``).
+
+    ``magnitudes=True`` appends a dict of the same four shapes holding, for
+    each element, the sum of the absolute values of the terms a finite-
+    precision evaluation adds up (the quantity rounding-error bounds of
+    sums scale with; for tolerances only):
+
+        dv:  P^T |dO|
+        dps: sum_t |dO_rt| (P |V|)_rt          (bounds rowsum(dO * O) too)
+        dq:  scale (|dS| |K| + dps_mag_r * P |K|)
+        dk:  scale (|dS|^T |Q| + P^T (dps_mag * |Q|))
+
+    The second terms carry an error of the row sum into dS = P (dP - D).
     """
     q, k, v, do = (np.asarray(t, dtype=np.float64) for t in (q, k, v, do))
     _check(q, k, v, do, mask_kind, kv_lens)
     B, H, N, d = q.shape
     scale = _as_scale(scale)
     causal = bool(mask_kind & MASK_CAUSAL)
+    rows = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
     units = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
     dQ, dK, dV = (np.full((B, H, N, d), np.nan) for _ in range(3))
     DP = np.full((B, H, N), np.nan)
+    M = ({"dq": np.full((B, H, N, d), np.nan), "dk": np.full((B, H, N, d), np.nan),
+          "dv": np.full((B, H, N, d), np.nan), "dps": np.full((B, H, N), np.nan)}
+         if magnitudes else None)
 
     def run(unit):
         b, h = unit
         n_vis = _n_vis(mask_kind, kv_lens, b, N)
+        mags = {} if magnitudes else None
         dQ[b, h], dK[b, h], dV[b, h], DP[b, h] = _head_bwd(
-            q[b, h], k[b, h], v[b, h], do[b, h], scale, causal, n_vis, row_block)
+            q[b, h], k[b, h], v[b, h], do[b, h], scale, causal, n_vis, rows, row_block, mags)
+        if magnitudes:
+            for name in M:
+                M[name][b, h] = mags[name]
 
     if workers <= 1 or len(units) == 1:
         for u in units:
@@ -151,6 +193,8 @@ def attention_bwd_ref(q, k, v, do, scale, mask_kind=0, kv_lens=None, heads=None,
         from threadpoolctl import threadpool_limits
         with threadpool_limits(1), ThreadPoolExecutor(workers) as ex:
             list(ex.map(run, units))
+    if magnitudes:
+        return dQ, dK, dV, DP, M
     return dQ, dK, dV, DP
 
 

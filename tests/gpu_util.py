@@ -76,3 +76,72 @@ def compare(O, L, Or, Lr, dtype, what=""):
         assert stats["o_relf"] <= tol["o_relf"], (what, stats)
     assert stats["lse_abs"] <= tol["lse_abs"], (what, stats)
     return stats
+
+
+# Backward tolerances (bf16 inputs, fp32 accumulation), per element: the
+# standard bound for a rounded sum of products, |err| <= k u (A + |ref|),
+# with u = 2^-8 the bf16 unit roundoff and A the sum of the absolute values
+# of the terms (the oracle's magnitudes).  The kernel rounds one factor of
+# every term to bf16 (P for dV, dS for dQ and dK: relative error <= u), the
+# row sum D inherits the bf16 rounding of O (magnitude terms of the oracle
+# carry it into dS), and the result is rounded once more (u |ref|); fp32
+# accumulation and the exp2/LSE errors are ~1e-6 relative, far below u.
+# k = 2 covers these with room.  An element whose terms are all zero (a key
+# nobody sees, a row that sees nothing) must come out exactly 0.  On the
+# named workloads (millions of elements, little cancellation in bulk) each
+# tensor's relative Frobenius error must also stay below 1e-2: independent
+# roundings give ~u/sqrt(3) ~ 2.3e-3 each, adding in quadrature.  Tiny cases
+# can be dominated by cancellation (two visible keys: dS_0 = -dS_1), where
+# that ratio says nothing and the element bound alone applies.
+U_BF16 = 2.0 ** -8
+TOL_BWD = {"k": 2.0, "relf": 1e-2}
+
+
+def run_bwd_gpu(x, scale, mask_kind, sentinel=True):
+    """Forward then backward on the GPU; returns fp64 dq, dk, dv, dp_rowsum
+    (and the forward's O, LSE)."""
+    import torch
+
+    import exact_attention_92_amd as fa
+    q, k, v, do = (to_dev(x[n]) for n in ("q", "k", "v", "do"))
+    kv = None
+    if x.get("kv_lens") is not None:
+        kv = torch.from_numpy(np.asarray(x["kv_lens"], dtype=np.int32)).cuda()
+    B, H, N, d = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    fa.fa_fwd(q, k, v, o, lse, scale, mask_kind, kv)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dps = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if sentinel:
+        for t in (dq, dk, dv, dps):
+            t.fill_(float("nan"))
+    fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, dps, scale, mask_kind, kv)
+    torch.cuda.synchronize()
+    return {"dq": o_to_f64(dq), "dk": o_to_f64(dk), "dv": o_to_f64(dv),
+            "dps": dps.cpu().numpy().astype(np.float64),
+            "o": o_to_f64(o), "lse": lse.cpu().numpy().astype(np.float64)}
+
+
+def compare_grads(g, ref, mag, what="", keys=("dq", "dk", "dv"), bulk=False):
+    """Assert backward parity of ``g`` against fp64 ``ref`` with the
+    per-element bound above (``mag``: the oracle's magnitudes)."""
+    stats = {}
+    for name in keys:
+        got, want, a = g[name], ref[name], mag[name]
+        assert not np.isnan(got).any(), f"{what}: {name} has unwritten (NaN) elements"
+        assert not np.isnan(want).any() and not np.isnan(a).any(), f"{what}: {name} reference"
+        err = np.abs(got - want)
+        bound = TOL_BWD["k"] * U_BF16 * (a + np.abs(want))
+        zero = bound == 0
+        assert np.all(err[zero] == 0.0), (what, name, "elements with no terms must be 0")
+        ratio = float(np.max(err[~zero] / bound[~zero], initial=0.0))
+        nrm = float(np.linalg.norm(want))
+        relf = float(np.linalg.norm(got - want) / nrm) if nrm > 0 else 0.0
+        stats[name] = (relf, ratio)
+        assert ratio <= 1.0, (what, name, "element bound", stats[name])
+        if bulk:
+            assert relf <= TOL_BWD["relf"], (what, name, "relative Frobenius", stats[name])
+    say(f"  {what}: " + " ".join(f"{n}: relF={a:.2e} err/bound={b:.2f}"
+                                 for n, (a, b) in stats.items()))
+    return stats

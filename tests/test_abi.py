@@ -26,7 +26,7 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared() == ["fa_fwd", "fa_fwd_f32", "fa_strerror"]
+    assert _declared() == ["fa_bwd", "fa_fwd", "fa_fwd_f32", "fa_strerror"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -68,6 +68,31 @@ def test_invalid_arguments_are_rejected_before_launch(lib, name):
     assert _call(lib, name, B=1 << 20, H=1 << 10, N=1 << 20) == bad  # grid too large
     assert _call(lib, name, d=96) == fa.FA_ERR_UNSUPPORTED
     assert _call(lib, name, d=256) == fa.FA_ERR_UNSUPPORTED
+
+
+def _bwd(lib, ptrs=None, B=1, H=1, N=16, d=64, scale=0.125, mask=0, kv=None):
+    ptrs = list(ptrs or [0x1000 * (i + 1) for i in range(10)])
+    return lib.fa_bwd(*[ctypes.c_void_p(p) if p is not None else None for p in ptrs], B, H, N, d,
+                      ctypes.c_float(scale), mask, ctypes.c_void_p(kv) if kv else None, None)
+
+
+def test_backward_invalid_arguments_are_rejected_before_launch(lib):
+    import exact_attention_92_amd as fa
+    bad = fa.FA_ERR_INVALID_ARG
+    good = [0x1000 * (i + 1) for i in range(10)]
+    for i in range(10):               # every pointer is required and 16-byte aligned
+        p = list(good)
+        p[i] = None
+        assert _bwd(lib, p) == bad, i
+        p[i] = good[i] + 4
+        assert _bwd(lib, p) == bad, i
+    assert _bwd(lib, B=0) == bad
+    assert _bwd(lib, N=0) == bad
+    assert _bwd(lib, mask=8) == bad
+    assert _bwd(lib, mask=fa.FA_MASK_KEY_PADDING) == bad
+    assert _bwd(lib, scale=float("-inf")) == bad
+    assert _bwd(lib, B=1 << 20, H=1 << 10, N=1 << 20) == bad
+    assert _bwd(lib, d=32) == fa.FA_ERR_UNSUPPORTED
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

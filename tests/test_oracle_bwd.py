@@ -247,6 +247,45 @@ def test_heads_subset_and_row_blocking_agree():
         assert np.array_equal(par[i], full[i])
 
 
+def test_row_subsets():
+    """Only the listed rows contribute: dQ and D are exact on them, and under
+    the causal mask the keys at or after the first row of a contiguous tail
+    get their complete dK and dV."""
+    N = 60
+    q, k, v, do = _rand(1, 2, N, 8, seed=21)
+    full = attention_bwd_ref(q, k, v, do, 0.3, MASK_CAUSAL)
+    rows = np.array([3, 17, 40, 59])
+    sub = attention_bwd_ref(q, k, v, do, 0.3, MASK_CAUSAL, rows=rows, row_block=3)
+    assert np.max(np.abs(sub[0][:, :, rows] - full[0][:, :, rows])) <= 1e-13
+    assert np.max(np.abs(sub[3][:, :, rows] - full[3][:, :, rows])) <= 1e-13
+    others = np.setdiff1d(np.arange(N), rows)
+    assert np.isnan(sub[0][:, :, others]).all() and np.isnan(sub[3][:, :, others]).all()
+    tail = np.arange(44, N)
+    sub = attention_bwd_ref(q, k, v, do, 0.3, MASK_CAUSAL, rows=tail)
+    for i in (1, 2):
+        assert np.max(np.abs(sub[i][:, :, 44:] - full[i][:, :, 44:])) <= 1e-13
+        assert not np.allclose(sub[i][:, :, :44], full[i][:, :, :44])
+
+
+@pytest.mark.parametrize("mask", MASKS)
+def test_magnitudes_bound_the_values(mask):
+    """Each magnitude is a sum of |terms|, so it bounds |value| (triangle
+    inequality), and equals it when every term is non-negative; asking for
+    them changes no value."""
+    q, k, v, do = _rand(2, 2, 41, 8, seed=22)
+    kv = np.array([0, 30], dtype=np.int32)
+    base = attention_bwd_ref(q, k, v, do, 0.3, mask, kv)
+    *vals, mags = attention_bwd_ref(q, k, v, do, 0.3, mask, kv, magnitudes=True, row_block=9)
+    for i, name in enumerate(("dq", "dk", "dv", "dps")):
+        assert np.max(np.abs(vals[i] - base[i])) <= 1e-12
+        assert np.all(mags[name] >= np.abs(vals[i]) * (1 - 1e-12) - 1e-300), name
+    # dO >= 0 and V >= 0: every term of dV and of rowsum(dO * O) is >= 0.
+    *vals, mags = attention_bwd_ref(q, k, np.abs(v), np.abs(do), 0.3, mask, kv,
+                                    magnitudes=True)
+    assert np.max(np.abs(mags["dv"] - vals[2])) <= 1e-12
+    assert np.max(np.abs(mags["dps"] - vals[3])) <= 1e-12
+
+
 def test_rejects_bad_arguments():
     q, k, v, do = _rand(1, 1, 4, 2, seed=20)
     with pytest.raises(ValueError):
