@@ -1,13 +1,18 @@
 #!/usr/bin/env python3
-"""Throughput of the exact attention forward on one MI355X.
+"""Throughput of the exact attention forward (or backward) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--pass fwd|bwd]
 
 One step = one fa_fwd call over the whole batch of the workload (default:
 B=2, H=32, N=4096, d=128, bf16, causal), inputs already resident in device
 memory.  Prints ONE JSON line with the throughput (FLOPs by 4*B*H*N^2*d,
 halved for causal), the roofline figures of the kernel, and the CPU oracle
 timed on the host as a reported baseline.
+
+``--pass bwd`` times one fa_bwd call per step instead (the forward runs once,
+untimed, to produce O and LSE); FLOPs are counted as the five products of the
+gradient, 2.5x the forward's.
 """
 import argparse
 import hashlib
@@ -23,28 +28,35 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "fwd attention TFLOP/s (bf16, N=4096 d=128 causal) and % of MFMA peak"
+METRIC_BWD = "bwd attention TFLOP/s (bf16, N=4096 d=128 causal) and % of MFMA peak"
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA peaks
-KERNEL_SRC = os.path.join(ROOT, "exact_attention_92_amd", "csrc", "fa_fwd.hip")
-PMC_SUMMARY = os.path.join(ROOT, "profiles", "fa_fwd_bf16_b2h32_n4096_d128_causal_pmc.md")
+CSRC = os.path.join(ROOT, "exact_attention_92_amd", "csrc")
+# Sources each pass's kernels are built from (the PMC summaries record their hash).
+KERNEL_SRCS = {"fwd": ["fa_fwd.hip"], "bwd": ["fa_bwd.hip", "fa_device.h"]}
+PMC_SUMMARY = {"fwd": os.path.join(ROOT, "profiles", "fa_fwd_bf16_b2h32_n4096_d128_causal_pmc.md"),
+               "bwd": os.path.join(ROOT, "profiles", "fa_bwd_bf16_b2h32_n4096_d128_causal_pmc.md")}
 
 
-def kernel_source_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_source_hash(which="fwd"):
+    h = hashlib.sha256()
+    for name in KERNEL_SRCS[which]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(which="fwd"):
     """HBM bytes per launch from the committed PMC summary, if it was taken on
     the current kernel source; otherwise None."""
     try:
-        text = open(PMC_SUMMARY).read()
+        text = open(PMC_SUMMARY[which]).read()
     except OSError:
         return None
     m = re.search(r"```json\s*(\{.*?\})\s*```", text, re.S)
     if not m:
         return None
     rec = json.loads(m.group(1))
-    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash(which):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -68,6 +80,26 @@ def cpu_baseline(x, wl, o_gpu):
                       f"{cores} worker threads with single-threaded BLAS"}, parity
 
 
+def cpu_baseline_bwd(x, wl, g):
+    """Time the backward oracle on the host (all heads) and check the GPU
+    gradients against it on the same bytes."""
+    from fa_inputs import to_f64
+    from oracle import attention_bwd_ref
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    q, k, v, do = (to_f64(x[n]) for n in ("q", "k", "v", "do"))
+    t0 = time.perf_counter()
+    ref = attention_bwd_ref(q, k, v, do, wl.scale, wl.mask_kind, x["kv_lens"], workers=cores)
+    dt = time.perf_counter() - t0
+    parity = {}
+    for name, want in zip(("dq", "dk", "dv"), ref[:3]):
+        parity[f"{name}_rel_frobenius"] = float(np.linalg.norm(g[name] - want) /
+                                                np.linalg.norm(want))
+    return {"value": wl.bwd_flops() / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "sample": f"the whole workload ({wl.B * wl.H} heads, all rows), fp64 NumPy/BLAS, "
+                      f"{cores} worker threads with single-threaded BLAS"}, parity
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -75,6 +107,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run 3 plain device copies of this many MiB (a known-size "
                          "reference for HBM byte counters)")
@@ -87,7 +120,7 @@ def main():
     import torch
 
     import exact_attention_92_amd as fa
-    from fa_inputs import BENCH_WORKLOAD, WORKLOADS, bf16_bits_to_f32, make_inputs
+    from fa_inputs import BENCH_WORKLOAD, WORKLOADS, bf16_bits_to_f32, make_bwd_inputs, make_inputs
 
     if args.copy_mib > 0:
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device="cuda:0")
@@ -98,7 +131,11 @@ def main():
         del src, dst
 
     wl = WORKLOADS[args.workload or BENCH_WORKLOAD]
-    x = make_inputs(wl)
+    bwd = args.which == "bwd"
+    if bwd and wl.dtype != "bf16":
+        print("--pass bwd runs the bf16 backward; pick a bf16 workload", file=sys.stderr)
+        sys.exit(2)
+    x = make_bwd_inputs(wl) if bwd else make_inputs(wl)
     dev = torch.device("cuda:0")
 
     def up(a):
@@ -115,6 +152,17 @@ def main():
 
     def step():
         fn(q, k, v, o, lse, wl.scale, wl.mask_kind, kv, stream.cuda_stream)
+
+    if bwd:
+        # The forward runs once (untimed) to give O and LSE; a step is fa_bwd.
+        step()
+        do = up(x["do"])
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        dps = torch.empty((wl.B, wl.H, wl.N), dtype=torch.float32, device=dev)
+
+        def step():
+            fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, dps, wl.scale, wl.mask_kind, kv,
+                      stream.cuda_stream)
 
     for _ in range(args.warmup):
         step()
@@ -139,13 +187,16 @@ def main():
     ms_per_step = total_ms / args.steps
     avg_launch_ms = float(np.mean(launch_ms))
 
-    flops = wl.flops()
+    flops = wl.bwd_flops() if bwd else wl.flops()
     value = flops / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
-    traffic = measured_traffic() if wl.name == BENCH_WORKLOAD else None
+    traffic = measured_traffic(args.which) if wl.name == BENCH_WORKLOAD else None
+    metric = METRIC_BWD if bwd else METRIC
+    if wl.name != BENCH_WORKLOAD:
+        metric = f"{args.which} attention TFLOP/s ({wl.name})"
     rec = {
-        "metric": METRIC if wl.name == BENCH_WORKLOAD else f"fwd attention TFLOP/s ({wl.name})",
+        "metric": metric,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -169,7 +220,19 @@ def main():
                      "min_launch_us": round(min(launch_ms) * 1e3, 2)},
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if bwd:
+        rec["pass"] = "bwd"
+        rec["roofline"]["kernel"] = "fa_bwd_dq_kernel + fa_bwd_dkdv_kernel (one fa_bwd call)"
+        # The kernels execute 7 products (S and dP are formed in both), the
+        # metric credits the 5 of the gradient.
+        rec["roofline"]["executed_mfma_tflops"] = round(achieved * 7 / 5, 2)
+    if not args.no_cpu_baseline and bwd:
+        g = {}
+        for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+            bits = t.view(torch.int16).cpu().numpy().view(np.uint16)
+            g[name] = bf16_bits_to_f32(bits).astype(np.float64)
+        rec["cpu_baseline"], rec["parity_vs_oracle"] = cpu_baseline_bwd(x, wl, g)
+    elif not args.no_cpu_baseline:
         if wl.dtype == "bf16":
             bits = o.view(torch.int16).cpu().numpy().view(np.uint16)
             o_host = bf16_bits_to_f32(bits).astype(np.float64)

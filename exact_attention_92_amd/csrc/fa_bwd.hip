@@ -279,6 +279,15 @@ void fa_bwd_dq_kernel(BwdParams p) {
 // dK, dV: one workgroup = 4 waves x 32 keys of one (batch, head)
 // ---------------------------------------------------------------------------
 constexpr int kKvWaves = 4;
+#ifndef FA_BWD_RA1
+#define FA_BWD_RA1 8    // LDS reads issued ahead in the S / dP products
+#endif
+#ifndef FA_BWD_PRE
+#define FA_BWD_PRE 16   // dV / dK operands read before the softmax work
+#endif
+#ifndef FA_BWD_RA2
+#define FA_BWD_RA2 8    // LDS reads issued ahead in the dV / dK products
+#endif
 
 template <int D>
 __global__ __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -446,6 +455,18 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
           const u32x4_t a2 = *(const u32x4_t*)&do_lds[buf][32 * qt + qperm][16 * ks + 8 * hf];
           dp[qt] = mfma_bf16(a2, vr[ks], dp[qt]);
         }
+      if (FA_BWD_RA1 > 0) mfma_read_ahead<2 * KS * QT, FA_BWD_RA1>();
+      // The first operands of the dV / dK products are requested now so they
+      // arrive while the softmax runs.  Operand i: chunk pc = i / (2 DT),
+      // tile dt = (i / 2) % DT, dO^T for even i and Q^T for odd i.
+      constexpr int PRE = FA_BWD_PRE;
+      u32x4_t apre[PRE > 0 ? PRE : 1];
+#pragma unroll
+      for (int i = 0; i < PRE; ++i) {
+        const int pc = i / (2 * DT), dt = (i / 2) % DT;
+        apre[i] = (i & 1) ? *(const u32x4_t*)&qt_lds[buf][32 * dt + n][16 * pc + 8 * hf]
+                          : *(const u32x4_t*)&dot_lds[buf][32 * dt + n][16 * pc + 8 * hf];
+      }
       // Hidden pairs: key past kv_len, or (causal) key after the query.
       const bool edge = (causal && q0 < kw0 + 31) || (kw0 + 31 >= n_vis);
       if (edge) {
@@ -486,11 +507,17 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
       for (int pc = 0; pc < PC; ++pc)
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
-          const u32x4_t a = *(const u32x4_t*)&dot_lds[buf][32 * dt + n][16 * pc + 8 * hf];
+          const int i = 2 * (pc * DT + dt);
+          const u32x4_t a = i < PRE ? apre[i < PRE ? i : 0]
+                                    : *(const u32x4_t*)&dot_lds[buf][32 * dt + n][16 * pc + 8 * hf];
           dva[dt] = mfma_bf16(a, pb[pc], dva[dt]);
-          const u32x4_t a2 = *(const u32x4_t*)&qt_lds[buf][32 * dt + n][16 * pc + 8 * hf];
+          const u32x4_t a2 = i + 1 < PRE ? apre[i + 1 < PRE ? i + 1 : 0]
+                                         : *(const u32x4_t*)&qt_lds[buf][32 * dt + n][16 * pc + 8 * hf];
           dka[dt] = mfma_bf16(a2, dsb[pc], dka[dt]);
         }
+      constexpr int NM2 = 2 * PC * DT;
+      if (FA_BWD_RA2 > 0)
+        mfma_read_ahead<NM2, (NM2 - PRE < FA_BWD_RA2 ? NM2 - PRE : FA_BWD_RA2)>();
     }
     if (more) store_block(buf ^ 1);
     __syncthreads();
