@@ -283,10 +283,13 @@ constexpr int kKvWaves = 4;
 #define FA_BWD_RA1 8    // LDS reads issued ahead in the S / dP products
 #endif
 #ifndef FA_BWD_PRE
-#define FA_BWD_PRE 16   // dV / dK operands read before the softmax work
+#define FA_BWD_PRE 0    // dV / dK operands read before the softmax work
 #endif
 #ifndef FA_BWD_RA2
 #define FA_BWD_RA2 8    // LDS reads issued ahead in the dV / dK products
+#endif
+#ifndef FA_BWD_LATE_LOAD
+#define FA_BWD_LATE_LOAD 1   // issue the next block's global loads after the softmax
 #endif
 
 template <int D>
@@ -432,7 +435,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   for (int i = qb0; i < nqb; ++i) {
     const int buf = (i - qb0) & 1;
     const bool more = i + 1 < nqb;
-    if (more) load_block(i + 1);
+    if (!FA_BWD_LATE_LOAD && more) load_block(i + 1);
     const int q0 = i * BQ;
     // Every key of this wave is hidden, or (causal) comes after every query
     // of the block.
@@ -501,6 +504,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
                                  p1 * (dp[qt][r0 + 2 * w + 1] - dv[2 * w + 1]));
         }
       }
+      if (FA_BWD_LATE_LOAD && more) load_block(i + 1);
       // dV^T += dO_i^T P and dK^T += Q_i^T dS: A operands are rows 32dt + n of
       // the transposed tiles, queries 16pc + 8hf + 0..7.
 #pragma unroll
@@ -518,6 +522,8 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
       constexpr int NM2 = 2 * PC * DT;
       if (FA_BWD_RA2 > 0)
         mfma_read_ahead<NM2, (NM2 - PRE < FA_BWD_RA2 ? NM2 - PRE : FA_BWD_RA2)>();
+    } else if (FA_BWD_LATE_LOAD && more) {
+      load_block(i + 1);
     }
     if (more) store_block(buf ^ 1);
     __syncthreads();
