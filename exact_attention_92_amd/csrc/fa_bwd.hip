@@ -279,18 +279,114 @@ void fa_bwd_dq_kernel(BwdParams p) {
 // dK, dV: one workgroup = 4 waves x 32 keys of one (batch, head)
 // ---------------------------------------------------------------------------
 constexpr int kKvWaves = 4;
-#ifndef FA_BWD_RA1
-#define FA_BWD_RA1 8    // LDS reads issued ahead in the S / dP products
-#endif
-#ifndef FA_BWD_PRE
-#define FA_BWD_PRE 0    // dV / dK operands read before the softmax work
-#endif
-#ifndef FA_BWD_RA2
-#define FA_BWD_RA2 8    // LDS reads issued ahead in the dV / dK products
-#endif
-#ifndef FA_BWD_LATE_LOAD
-#define FA_BWD_LATE_LOAD 1   // issue the next block's global loads after the softmax
-#endif
+
+// Global -> register staging of one block of BQ query rows for the dK/dV
+// kernel: pieces of 4 rows x 8 dims of Q (sign-flipped when scale < 0) and
+// dO, plus LSE (log2 units) or D for one row per thread of the first 2 BQ.
+struct KvStage {
+  rsrc_t rq, rdo;
+  rsrc_t rl, rd;      // this head's LSE and D rows (N floats each)
+  uint32_t u_off;     // byte offset of this thread's piece within a block
+  unsigned qsign;
+  int N, tid;
+  bool unit;          // this thread stages a Q/dO piece
+};
+
+// Branch-free: threads with nothing to load use an offset past the end of
+// the buffer range (2^31 is beyond any accepted size), which reads zeros.
+template <int D, int BQ>
+__device__ __forceinline__ void kv_stage_load(const KvStage& g, int i, u32x4_t (&qreg)[4],
+                                              u32x4_t (&dreg)[4], float& sreg) {
+  constexpr uint32_t ROWB = D * 2;
+  constexpr uint32_t kOut = 0x80000000u;
+  const uint32_t off = g.unit ? (uint32_t)(i * BQ) * ROWB + g.u_off : kOut;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    qreg[t] = buf_load16(g.rq, off + t * ROWB) ^ g.qsign;
+    dreg[t] = buf_load16(g.rdo, off + t * ROWB);
+  }
+  const int row = i * BQ + (g.tid % BQ);
+  const bool ok = row < g.N;
+  const float l = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+      g.rl, (ok && g.tid < BQ) ? 4u * row : kOut, 0, 0));
+  const float d = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+      g.rd, (ok && g.tid >= BQ && g.tid < 2 * BQ) ? 4u * row : kOut, 0, 0));
+  sreg = g.tid < BQ ? lse_log2(l, ok) : d;
+}
+
+// One block of BQ query rows for one wave's 32 keys: S = Q K^T and
+// dP = dO V^T (one key per lane, query rows permuted so register r of tile qt
+// holds query q0 + 32qt + 16(r/8) + 8hf + r%8), P = 2^(s c - LSE2),
+// dS = P (dP - D), then dV^T += dO^T P and dK^T += Q^T dS.  EDGE: the block
+// holds hidden pairs (key past kv_len, or causal key after query); the other
+// blocks skip the mask.  The next block's global loads are issued after the
+// softmax, when the scores no longer occupy registers.  The body is one
+// straight-line region (the staging loads are branch-free).
+template <int D, int BQ, bool EDGE>
+__device__ __forceinline__ void kv_block(
+    const uint16_t (*q_rows)[D + 8], const uint16_t (*do_rows)[D + 8],
+    const uint16_t (*q_cols)[BQ + 8], const uint16_t (*do_cols)[BQ + 8], const float* l_vec,
+    const float* d_vec, const u32x4_t (&kr)[D / 16], const u32x4_t (&vr)[D / 16],
+    f32x16_t (&dva)[D / 32], f32x16_t (&dka)[D / 32], const KvStage& g, int inext,
+    u32x4_t (&qreg)[4], u32x4_t (&dreg)[4], float& sreg, int q0, int key, int n_vis,
+    bool causal, float c, int n, int hf, int qperm) {
+  constexpr int KS = D / 16, DT = D / 32, QT = BQ / 32, PC = BQ / 16;
+  f32x16_t s[QT], dp[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    s[qt] = zero16();
+    dp[qt] = zero16();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4_t a = *(const u32x4_t*)&q_rows[32 * qt + qperm][16 * ks + 8 * hf];
+      s[qt] = mfma_bf16(a, kr[ks], s[qt]);
+      const u32x4_t a2 = *(const u32x4_t*)&do_rows[32 * qt + qperm][16 * ks + 8 * hf];
+      dp[qt] = mfma_bf16(a2, vr[ks], dp[qt]);
+    }
+  }
+  if constexpr (EDGE) {
+    const bool hidden_key = key >= n_vis;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qi = q0 + 32 * qt + 16 * (r >> 3) + 8 * hf + (r & 7);
+        if (hidden_key || (causal && key > qi)) s[qt][r] = -INFINITY;
+      }
+  }
+  // Chunk pc of 16 queries = registers 8(pc%2).. of tile pc/2.
+  u32x4_t pb[PC], dsb[PC];
+#pragma unroll
+  for (int pc = 0; pc < PC; ++pc) {
+    const int qt = pc >> 1, r0 = 8 * (pc & 1);
+    const float4* lp = (const float4*)&l_vec[16 * pc + 8 * hf];
+    const float4* dpp = (const float4*)&d_vec[16 * pc + 8 * hf];
+    const float4 la = lp[0], lb = lp[1], da = dpp[0], db = dpp[1];
+    const float lv[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
+    const float dv[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qt][r0 + 2 * w], c, -lv[2 * w]));
+      const float p1 =
+          __builtin_amdgcn_exp2f(__builtin_fmaf(s[qt][r0 + 2 * w + 1], c, -lv[2 * w + 1]));
+      pb[pc][w] = pack_bf16(p0, p1);
+      dsb[pc][w] = pack_bf16(p0 * (dp[qt][r0 + 2 * w] - dv[2 * w]),
+                             p1 * (dp[qt][r0 + 2 * w + 1] - dv[2 * w + 1]));
+    }
+  }
+  // Past the last block the loads read zeros and rows past N; unused.
+  kv_stage_load<D, BQ>(g, inext, qreg, dreg, sreg);
+  // A operands: rows 32dt + n of the transposed tiles, queries 16pc + 8hf + 0..7.
+#pragma unroll
+  for (int pc = 0; pc < PC; ++pc)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const u32x4_t a = *(const u32x4_t*)&do_cols[32 * dt + n][16 * pc + 8 * hf];
+      dva[dt] = mfma_bf16(a, pb[pc], dva[dt]);
+      const u32x4_t a2 = *(const u32x4_t*)&q_cols[32 * dt + n][16 * pc + 8 * hf];
+      dka[dt] = mfma_bf16(a2, dsb[pc], dka[dt]);
+    }
+}
 
 template <int D>
 __global__ __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -377,22 +473,16 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   const float* Dh = p.dps + (size_t)bh * N;
   u32x4_t qreg[4], dreg[4];
   float sreg = 0.f;
-  auto load_block = [&](int i) {
-    const uint32_t base = (uint32_t)(i * BQ) * ROWB;
-    if (st_unit) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        qreg[t] = buf_load16(rq, base + u_off + t * ROWB) ^ p.qsign;
-        dreg[t] = buf_load16(rdo, base + u_off + t * ROWB);
-      }
-    }
-    if (tid < 2 * BQ) {
-      const int row = i * BQ + (tid % BQ);
-      const bool ok = row < N;
-      if (tid < BQ) sreg = lse_log2(ok ? Lh[row] : 0.f, ok);
-      else sreg = ok ? Dh[row] : 0.f;
-    }
-  };
+  KvStage g;
+  g.rq = rq;
+  g.rdo = rdo;
+  g.rl = make_rsrc(Lh, (uint32_t)N * 4u);
+  g.rd = make_rsrc(Dh, (uint32_t)N * 4u);
+  g.u_off = u_off;
+  g.qsign = p.qsign;
+  g.N = N;
+  g.tid = tid;
+  g.unit = st_unit;
   auto store_block = [&](int buf) {
     if (st_unit) {
       u32x2_t lo[4], hi[4];
@@ -427,105 +517,29 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   const int qperm = row_perm(n);
 
   if (qb0 < nqb) {
-    load_block(qb0);
+    kv_stage_load<D, BQ>(g, qb0, qreg, dreg, sreg);
     store_block(0);
   }
   __syncthreads();
 
   for (int i = qb0; i < nqb; ++i) {
     const int buf = (i - qb0) & 1;
-    const bool more = i + 1 < nqb;
-    if (!FA_BWD_LATE_LOAD && more) load_block(i + 1);
     const int q0 = i * BQ;
     // Every key of this wave is hidden, or (causal) comes after every query
-    // of the block.
+    // of the block: nothing to add, only the staging goes on.
     const bool wave_skip = kw0 >= n_vis || (causal && q0 + BQ - 1 < kw0);
-    if (!wave_skip) {
-      // S = Q_i K^T and dP = dO_i V^T with query rows permuted: register r
-      // of tile qt holds query q0 + 32qt + 16(r/8) + 8hf + r%8; column = key.
-      f32x16_t s[QT], dp[QT];
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        s[qt] = zero16();
-        dp[qt] = zero16();
-      }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-          const u32x4_t a = *(const u32x4_t*)&q_lds[buf][32 * qt + qperm][16 * ks + 8 * hf];
-          s[qt] = mfma_bf16(a, kr[ks], s[qt]);
-          const u32x4_t a2 = *(const u32x4_t*)&do_lds[buf][32 * qt + qperm][16 * ks + 8 * hf];
-          dp[qt] = mfma_bf16(a2, vr[ks], dp[qt]);
-        }
-      if (FA_BWD_RA1 > 0) mfma_read_ahead<2 * KS * QT, FA_BWD_RA1>();
-      // The first operands of the dV / dK products are requested now so they
-      // arrive while the softmax runs.  Operand i: chunk pc = i / (2 DT),
-      // tile dt = (i / 2) % DT, dO^T for even i and Q^T for odd i.
-      constexpr int PRE = FA_BWD_PRE;
-      u32x4_t apre[PRE > 0 ? PRE : 1];
-#pragma unroll
-      for (int i = 0; i < PRE; ++i) {
-        const int pc = i / (2 * DT), dt = (i / 2) % DT;
-        apre[i] = (i & 1) ? *(const u32x4_t*)&qt_lds[buf][32 * dt + n][16 * pc + 8 * hf]
-                          : *(const u32x4_t*)&dot_lds[buf][32 * dt + n][16 * pc + 8 * hf];
-      }
-      // Hidden pairs: key past kv_len, or (causal) key after the query.
-      const bool edge = (causal && q0 < kw0 + 31) || (kw0 + 31 >= n_vis);
-      if (edge) {
-        const bool hidden_key = key >= n_vis;
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int qi = q0 + 32 * qt + 16 * (r >> 3) + 8 * hf + (r & 7);
-            if (hidden_key || (causal && key > qi)) s[qt][r] = -INFINITY;
-          }
-      }
-      // P = 2^(s c - LSE2) and dS = P (dP - D), packed to bf16 as chunks of
-      // 16 queries (chunk pc = registers 8(pc%2).. of tile pc/2).
-      u32x4_t pb[PC], dsb[PC];
-#pragma unroll
-      for (int pc = 0; pc < PC; ++pc) {
-        const int qt = pc >> 1, r0 = 8 * (pc & 1);
-        const float4* lp = (const float4*)&l_lds[buf][16 * pc + 8 * hf];
-        const float4* dpp = (const float4*)&d_lds[buf][16 * pc + 8 * hf];
-        const float4 la = lp[0], lb = lp[1], da = dpp[0], db = dpp[1];
-        const float lv[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
-        const float dv[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float p0 =
-              __builtin_amdgcn_exp2f(__builtin_fmaf(s[qt][r0 + 2 * w], c, -lv[2 * w]));
-          const float p1 =
-              __builtin_amdgcn_exp2f(__builtin_fmaf(s[qt][r0 + 2 * w + 1], c, -lv[2 * w + 1]));
-          pb[pc][w] = pack_bf16(p0, p1);
-          dsb[pc][w] = pack_bf16(p0 * (dp[qt][r0 + 2 * w] - dv[2 * w]),
-                                 p1 * (dp[qt][r0 + 2 * w + 1] - dv[2 * w + 1]));
-        }
-      }
-      if (FA_BWD_LATE_LOAD && more) load_block(i + 1);
-      // dV^T += dO_i^T P and dK^T += Q_i^T dS: A operands are rows 32dt + n of
-      // the transposed tiles, queries 16pc + 8hf + 0..7.
-#pragma unroll
-      for (int pc = 0; pc < PC; ++pc)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const int i = 2 * (pc * DT + dt);
-          const u32x4_t a = i < PRE ? apre[i < PRE ? i : 0]
-                                    : *(const u32x4_t*)&dot_lds[buf][32 * dt + n][16 * pc + 8 * hf];
-          dva[dt] = mfma_bf16(a, pb[pc], dva[dt]);
-          const u32x4_t a2 = i + 1 < PRE ? apre[i + 1 < PRE ? i + 1 : 0]
-                                         : *(const u32x4_t*)&qt_lds[buf][32 * dt + n][16 * pc + 8 * hf];
-          dka[dt] = mfma_bf16(a2, dsb[pc], dka[dt]);
-        }
-      constexpr int NM2 = 2 * PC * DT;
-      if (FA_BWD_RA2 > 0)
-        mfma_read_ahead<NM2, (NM2 - PRE < FA_BWD_RA2 ? NM2 - PRE : FA_BWD_RA2)>();
-    } else if (FA_BWD_LATE_LOAD && more) {
-      load_block(i + 1);
-    }
-    if (more) store_block(buf ^ 1);
+    const bool edge = (causal && q0 < kw0 + 31) || (kw0 + 31 >= n_vis);
+    if (wave_skip)
+      kv_stage_load<D, BQ>(g, i + 1, qreg, dreg, sreg);
+    else if (edge)
+      kv_block<D, BQ, true>(q_lds[buf], do_lds[buf], qt_lds[buf], dot_lds[buf], l_lds[buf],
+                            d_lds[buf], kr, vr, dva, dka, g, i + 1, qreg, dreg, sreg, q0, key,
+                            n_vis, causal, c, n, hf, qperm);
+    else
+      kv_block<D, BQ, false>(q_lds[buf], do_lds[buf], qt_lds[buf], dot_lds[buf], l_lds[buf],
+                             d_lds[buf], kr, vr, dva, dka, g, i + 1, qreg, dreg, sreg, q0, key,
+                             n_vis, causal, c, n, hf, qperm);
+    if (i + 1 < nqb) store_block(buf ^ 1);
     __syncthreads();
   }
 

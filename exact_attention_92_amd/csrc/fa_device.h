@@ -86,19 +86,6 @@ __device__ __forceinline__ void transpose4x8(const u32x4_t (&x)[4], u32x2_t (&ou
   }
 }
 
-// Scheduling hint for a run of NM MFMAs, each fed by one LDS operand read:
-// issue AHEAD reads first, then alternate MFMA and read.  An LDS round trip
-// under load spans about ten MFMA issue intervals, so reads must run ahead.
-template <int NM, int AHEAD>
-__device__ __forceinline__ void mfma_read_ahead() {
-  if (AHEAD > 0) __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);
-#pragma unroll
-  for (int i = 0; i < NM; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (i + AHEAD < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-}
-
 // Workgroups are dispatched round-robin over the 8 XCDs (w % 8), in order
 // within one.  Maps the linear workgroup id to (head, block) so that when the
 // heads split evenly XCD x owns a contiguous range of heads (their tensors
