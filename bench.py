@@ -29,12 +29,14 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fwd attention TFLOP/s (bf16, N=4096 d=128 causal) and % of MFMA peak"
 METRIC_BWD = "bwd attention TFLOP/s (bf16, N=4096 d=128 causal) and % of MFMA peak"
-PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA peaks
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "fp8": 5000.0}   # MI355X dense MFMA peaks
 CSRC = os.path.join(ROOT, "exact_attention_92_amd", "csrc")
 # Sources each pass's kernels are built from (the PMC summaries record their hash).
-KERNEL_SRCS = {"fwd": ["fa_fwd.hip"], "bwd": ["fa_bwd.hip", "fa_device.h"]}
+KERNEL_SRCS = {"fwd": ["fa_fwd.hip"], "bwd": ["fa_bwd.hip", "fa_device.h"],
+               "fp8": ["fa_fwd_fp8.hip", "fa_device.h"]}
 PMC_SUMMARY = {"fwd": os.path.join(ROOT, "profiles", "fa_fwd_bf16_b2h32_n4096_d128_causal_pmc.md"),
-               "bwd": os.path.join(ROOT, "profiles", "fa_bwd_bf16_b2h32_n4096_d128_causal_pmc.md")}
+               "bwd": os.path.join(ROOT, "profiles", "fa_bwd_bf16_b2h32_n4096_d128_causal_pmc.md"),
+               "fp8": os.path.join(ROOT, "profiles", "fa_fwd_fp8_b2h32_n4096_d128_causal_pmc.md")}
 
 
 def kernel_source_hash(which="fwd"):
@@ -64,10 +66,10 @@ def measured_traffic(which="fwd"):
 def cpu_baseline(x, wl, o_gpu):
     """Time the oracle on the host (all heads of the workload) and check the
     GPU output against it on the same bytes."""
-    from fa_inputs import to_f64
+    from fa_inputs import inputs_f64
     from oracle import attention_ref
     cores = max(1, min(16, len(os.sched_getaffinity(0))))
-    q, k, v = (to_f64(x[n]) for n in "qkv")
+    q, k, v = inputs_f64(x)
     t0 = time.perf_counter()
     Or, Lr = attention_ref(q, k, v, wl.scale, wl.mask_kind, x["kv_lens"], workers=cores)
     dt = time.perf_counter() - t0
@@ -120,7 +122,8 @@ def main():
     import torch
 
     import exact_attention_92_amd as fa
-    from fa_inputs import BENCH_WORKLOAD, WORKLOADS, bf16_bits_to_f32, make_bwd_inputs, make_inputs
+    from fa_inputs import (BENCH_WORKLOAD, FP8_WORKLOADS, WORKLOADS, bf16_bits_to_f32,
+                           make_bwd_inputs, make_inputs)
 
     if args.copy_mib > 0:
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device="cuda:0")
@@ -130,7 +133,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    wl = WORKLOADS[args.workload or BENCH_WORKLOAD]
+    wl = {**WORKLOADS, **FP8_WORKLOADS}[args.workload or BENCH_WORKLOAD]
     bwd = args.which == "bwd"
     if bwd and wl.dtype != "bf16":
         print("--pass bwd runs the bf16 backward; pick a bf16 workload", file=sys.stderr)
@@ -145,13 +148,22 @@ def main():
 
     q, k, v = up(x["q"]), up(x["k"]), up(x["v"])
     kv = None if x["kv_lens"] is None else torch.from_numpy(x["kv_lens"]).to(dev)
-    o = torch.empty_like(q)
+    shape = (wl.B, wl.H, wl.N, wl.d)
+    o = torch.empty(shape, dtype=torch.float32 if wl.dtype == "f32" else torch.bfloat16,
+                    device=dev)
     lse = torch.empty((wl.B, wl.H, wl.N), dtype=torch.float32, device=dev)
-    fn = fa.fa_fwd if wl.dtype == "bf16" else fa.fa_fwd_f32
     stream = torch.cuda.current_stream(dev)
+    if wl.dtype == "fp8":
+        qs, ks, vs = (up(x[n + "_descale"]) for n in "qkv")
 
-    def step():
-        fn(q, k, v, o, lse, wl.scale, wl.mask_kind, kv, stream.cuda_stream)
+        def step():
+            fa.fa_fwd_fp8(q, k, v, qs, ks, vs, o, lse, wl.scale, wl.mask_kind, kv,
+                          stream.cuda_stream)
+    else:
+        fn = fa.fa_fwd if wl.dtype == "bf16" else fa.fa_fwd_f32
+
+        def step():
+            fn(q, k, v, o, lse, wl.scale, wl.mask_kind, kv, stream.cuda_stream)
 
     if bwd:
         # The forward runs once (untimed) to give O and LSE; a step is fa_bwd.
@@ -191,7 +203,9 @@ def main():
     value = flops / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[wl.dtype]
     achieved = flops / (avg_launch_ms * 1e-3) / 1e12
-    traffic = measured_traffic(args.which) if wl.name == BENCH_WORKLOAD else None
+    which = "fp8" if wl.dtype == "fp8" else args.which
+    traffic = (measured_traffic(which)
+               if wl.name in (BENCH_WORKLOAD, "fp8_b2h32_n4096_d128_causal") else None)
     metric = METRIC_BWD if bwd else METRIC
     if wl.name != BENCH_WORKLOAD:
         metric = f"{args.which} attention TFLOP/s ({wl.name})"
@@ -215,7 +229,8 @@ def main():
                    "flops_per_step": flops, "device": torch.cuda.get_device_name(dev)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": "fa_fwd_bf16_kernel" if wl.dtype == "bf16" else "fa_fwd_f32_kernel",
+                     "kernel": {"bf16": "fa_fwd_bf16_kernel", "f32": "fa_fwd_f32_kernel",
+                                "fp8": "fa_fwd_fp8_kernel"}[wl.dtype],
                      "avg_launch_us": round(avg_launch_ms * 1e3, 2),
                      "min_launch_us": round(min(launch_ms) * 1e3, 2)},
         "cpu_baseline": None,
@@ -233,7 +248,7 @@ def main():
             g[name] = bf16_bits_to_f32(bits).astype(np.float64)
         rec["cpu_baseline"], rec["parity_vs_oracle"] = cpu_baseline_bwd(x, wl, g)
     elif not args.no_cpu_baseline:
-        if wl.dtype == "bf16":
+        if o.dtype == torch.bfloat16:
             bits = o.view(torch.int16).cpu().numpy().view(np.uint16)
             o_host = bf16_bits_to_f32(bits).astype(np.float64)
         else:

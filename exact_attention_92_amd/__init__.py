@@ -1,7 +1,8 @@
 """Exact attention on MI355X (gfx950): Python binding of libfa92.so.
 
 The binding only marshals arguments: every step of the forward and backward
-passes runs in the HIP kernels of ``csrc/fa_fwd.hip`` and ``csrc/fa_bwd.hip``.  PyTorch supplies device memory and
+passes runs in the HIP kernels of ``csrc/fa_fwd.hip``, ``csrc/fa_fwd_fp8.hip`` and
+``csrc/fa_bwd.hip``.  PyTorch supplies device memory and
 the stream.  There is no CPU or PyTorch fallback: if the library is missing
 or the GPU is absent, the calls raise.
 
@@ -10,6 +11,9 @@ Names follow the C ABI of ``include/fa_api.h``:
 * ``fa_fwd(q, k, v, o, lse, scale, mask_kind=0, kv_lens=None, stream=None)``
   -- bf16 tensors ``[B, H, N, d]``
 * ``fa_fwd_f32(...)`` -- the same with float32 tensors
+* ``fa_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, o, lse, scale,
+  mask_kind=0, kv_lens=None, stream=None)`` -- E4M3 codes (uint8 tensors)
+  with per-(batch, head) float32 scales; o is bf16
 * ``fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, dp_rowsum, scale, mask_kind=0,
   kv_lens=None, stream=None)`` -- bf16 gradients
 * ``fa_strerror(status)``
@@ -32,7 +36,7 @@ FA_ERR_UNSUPPORTED = -2
 FA_ERR_HIP = -3
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa92.so")
-EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_bwd", "fa_strerror")
+EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_bwd", "fa_strerror")
 
 _lib = None
 
@@ -58,6 +62,8 @@ def load_library():
         fn = getattr(lib, name)
         fn.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, vp]
         fn.restype = i32
+    lib.fa_fwd_fp8.argtypes = [vp] * 8 + [i32, i32, i32, i32, f32, i32, vp, vp]
+    lib.fa_fwd_fp8.restype = i32
     lib.fa_bwd.argtypes = [vp] * 10 + [i32, i32, i32, i32, f32, i32, vp, vp]
     lib.fa_bwd.restype = i32
     lib.fa_strerror.argtypes = [i32]
@@ -119,6 +125,39 @@ def _stream_handle(stream, device):
     if stream is None:
         return torch.cuda.current_stream(device).cuda_stream
     return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def fa_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, o, lse, scale, mask_kind=FA_MASK_NONE,
+               kv_lens=None, stream=None):
+    """E4M3 forward: q, k, v uint8 codes [B, H, N, d]; descales float32 [B, H];
+    writes o (bf16) and lse (float32)."""
+    import torch
+    lib = load_library()
+    for nm, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.uint8:
+            raise TypeError(f"{nm} must hold E4M3 codes as torch.uint8, got {t.dtype}")
+        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4 or t.shape != q.shape:
+            raise ValueError(f"{nm} must be a contiguous device tensor shaped like q")
+    B, H, N, d = q.shape
+    for nm, t in (("q_descale", q_descale), ("k_descale", k_descale), ("v_descale", v_descale)):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() \
+                or t.numel() != B * H:
+            raise ValueError(f"{nm} must be a contiguous float32 device tensor [B, H]")
+    if o.dtype != torch.bfloat16 or not o.is_cuda or not o.is_contiguous() \
+            or tuple(o.shape) != (B, H, N, d):
+        raise ValueError("o must be a contiguous bf16 device tensor [B, H, N, d]")
+    if lse.dtype != torch.float32 or not lse.is_cuda or not lse.is_contiguous() \
+            or tuple(lse.shape) != (B, H, N):
+        raise ValueError("lse must be a contiguous float32 device tensor [B, H, N]")
+    if kv_lens is not None:
+        if kv_lens.dtype != torch.int32 or not kv_lens.is_cuda or kv_lens.numel() != B:
+            raise ValueError("kv_lens must be an int32 device tensor [B]")
+    st = lib.fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(q_descale), _ptr(k_descale),
+                        _ptr(v_descale), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
+                        int(mask_kind), _ptr(kv_lens),
+                        ctypes.c_void_p(_stream_handle(stream, q.device)))
+    if st != FA_OK:
+        raise FaError(st, fa_strerror(st))
 
 
 def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, dp_rowsum, scale, mask_kind=FA_MASK_NONE,

@@ -15,6 +15,12 @@ Recipe (identical for every workload):
   round-to-nearest-even and keep them as uint16 bit patterns.
 * Key-padding workloads draw one valid key length per batch entry,
   uniform over the inclusive integer range ``kv_len_range``.
+* fp8 workloads quantize the same float32 draws to OCP FP8 E4M3 (the
+  "e4m3fn" encoding: 4 exponent bits with bias 7, 3 mantissa bits, largest
+  finite value 448, no infinities) with one float32 scale per (batch, head)
+  and tensor: descale = max|x| / 448 over that head's [N, d] values, code =
+  nearest E4M3 value of x / descale (ties to the even code).  The
+  dequantized value is code_value * descale.
 * The backward pass's upstream gradient dO (same shape as O) comes from a
   fifth stream, ``SeedSequence(seed).spawn(5)[4]`` (the first four children
   are the ones above, so the forward inputs do not change): float32
@@ -41,7 +47,7 @@ class Workload:
     H: int
     N: int
     d: int
-    dtype: str  # "f32" or "bf16"
+    dtype: str  # "f32", "bf16" or "fp8"
     mask_kind: int
     seed: int
     q_mult: float = 1.0
@@ -87,6 +93,13 @@ WORKLOADS = {
         note="long context, causal"),
 }
 
+# The fp8 counterpart of the bench workload: the same draws, quantized per head.
+FP8_WORKLOADS = {
+    "fp8_b2h32_n4096_d128_causal": Workload(
+        "fp8_b2h32_n4096_d128_causal", 2, 32, 4096, 128, "fp8", MASK_CAUSAL, seed=3,
+        q_mult=2.0, note="fp8 E4M3 Q, K, V with per-head scales; causal"),
+}
+
 # The workload the throughput figure is quoted on.
 BENCH_WORKLOAD = "bf16_b2h32_n4096_d128_causal"
 
@@ -113,6 +126,57 @@ def bf16_bits_to_f32(u: np.ndarray) -> np.ndarray:
     return (u.astype(np.uint32) << 16).view(np.float32)
 
 
+def _fp8_decode_code(c: int) -> float:
+    """Value of an E4M3 (e4m3fn) code with the sign bit clear (0..126)."""
+    e, m = c >> 3, c & 7
+    if e == 0:
+        return m * 2.0 ** -9               # subnormal: 2^-6 * m/8
+    return (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+# Non-negative E4M3 values by code 0..126 (0x7F is NaN); increasing in the code.
+_FP8_POS = np.array([_fp8_decode_code(c) for c in range(0x7F)], dtype=np.float64)
+FP8_MAX = 448.0
+
+
+def f32_to_fp8_e4m3(x: np.ndarray) -> np.ndarray:
+    """float -> E4M3 codes (uint8): the nearest representable value, ties to
+    the even code (the one whose mantissa ends in 0).  |x| above 448 is
+    clamped to 448 (the recipe scales values into range first).  An input
+    encoding step, not attention arithmetic."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), FP8_MAX)
+    hi = np.clip(np.searchsorted(_FP8_POS, a, side="left"), 0, len(_FP8_POS) - 1)
+    lo = np.maximum(hi - 1, 0)
+    dlo = a - _FP8_POS[lo]
+    dhi = _FP8_POS[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    neg = np.signbit(x)             # a negative value that rounds to 0 keeps its sign
+    return (code | (neg.astype(np.uint8) << 7)).astype(np.uint8)
+
+
+def fp8_e4m3_to_f64(u: np.ndarray) -> np.ndarray:
+    """E4M3 codes (uint8) -> exact float64 values (0x7F/0xFF decode as NaN)."""
+    u = np.asarray(u, dtype=np.uint8)
+    mag = np.concatenate([_FP8_POS, [np.nan]])[u & 0x7F]
+    return np.where(u & 0x80, -mag, mag)
+
+
+def quantize_fp8_per_head(x: np.ndarray):
+    """Per-(batch, head) E4M3 quantization of float32 [B, H, N, d]: returns
+    (codes uint8 [B, H, N, d], descale float32 [B, H])."""
+    amax = np.abs(x).max(axis=(2, 3)).astype(np.float32)
+    descale = np.where(amax > 0, amax / np.float32(FP8_MAX), np.float32(1.0)).astype(np.float32)
+    codes = f32_to_fp8_e4m3(x.astype(np.float64) / descale[:, :, None, None].astype(np.float64))
+    return codes, descale
+
+
+def dequant_fp8_f64(codes: np.ndarray, descale: np.ndarray) -> np.ndarray:
+    """Exact float64 values code_value * descale of per-head quantized data."""
+    return fp8_e4m3_to_f64(codes) * np.asarray(descale, dtype=np.float64)[:, :, None, None]
+
+
 def _streams(seed: int, n: int = 4):
     return [np.random.Generator(np.random.PCG64(s))
             for s in np.random.SeedSequence(seed).spawn(n)]
@@ -126,8 +190,8 @@ def make_raw(B: int, H: int, N: int, d: int, dtype: str, seed: int,
     uint16 bf16 bit patterns for ``"bf16"``) and ``kv_lens`` (int32 ``[B]`` or
     None).
     """
-    if dtype not in ("f32", "bf16"):
-        raise ValueError(f"dtype must be 'f32' or 'bf16', got {dtype!r}")
+    if dtype not in ("f32", "bf16", "fp8"):
+        raise ValueError(f"dtype must be 'f32', 'bf16' or 'fp8', got {dtype!r}")
     gq, gk, gv, gl = _streams(seed)
     shape = (B, H, N, d)
     q = gq.standard_normal(shape, dtype=np.float32)
@@ -141,6 +205,10 @@ def make_raw(B: int, H: int, N: int, d: int, dtype: str, seed: int,
         kv_lens = gl.integers(lo, hi, size=B, endpoint=True).astype(np.int32)
     if dtype == "bf16":
         q, k, v = f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+    if dtype == "fp8":
+        (q, qs), (k, ks), (v, vs) = (quantize_fp8_per_head(t) for t in (q, k, v))
+        return {"q": q, "k": k, "v": v, "kv_lens": kv_lens,
+                "q_descale": qs, "k_descale": ks, "v_descale": vs}
     return {"q": q, "k": k, "v": v, "kv_lens": kv_lens}
 
 
@@ -166,8 +234,17 @@ def make_bwd_inputs(wl: Workload):
     return x
 
 
+def inputs_f64(x: dict):
+    """Exact float64 Q, K, V of a generated input dict (any dtype)."""
+    if x["q"].dtype == np.uint8:
+        return tuple(dequant_fp8_f64(x[n], x[n + "_descale"]) for n in "qkv")
+    return tuple(to_f64(x[n]) for n in "qkv")
+
+
 def to_f64(x: np.ndarray) -> np.ndarray:
     """Exact float64 view of generated data (bf16 bit patterns or float32)."""
+    if x.dtype == np.uint8:
+        raise ValueError("fp8 codes need their scales: use inputs_f64 / dequant_fp8_f64")
     if x.dtype == np.uint16:
         return bf16_bits_to_f32(x).astype(np.float64)
     return np.asarray(x, dtype=np.float64)

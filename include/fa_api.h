@@ -91,6 +91,27 @@ int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int N, int d, float scale, int mask_kind,
                const int32_t* kv_lens, void* stream);
 
+/* FP8 forward (the FP8 path of "FlashAttention 完整解析" §5.5 and of the
+ * youngju.dev walkthrough §9.2): q, k, v hold OCP FP8 E4M3 codes
+ * ("e4m3fn": bias 7, largest finite 448, no infinities) of shape
+ * [B, H, N, d]; each (batch, head) has one float32 scale per tensor, so the
+ * values are q_code * q_descale[b*H + h] and likewise for k and v (block
+ * quantization with one block per head).  The result is the attention of
+ * those values, with the same mask, scale, LSE and empty-row conventions as
+ * fa_fwd; o is bfloat16 [B, H, N, d], lse float32 [B, H, N].
+ *  - Products run on the E4M3 matrix cores with float32 accumulation.  The
+ *    probabilities (each at most 1: the row max is exact) are multiplied by
+ *    448 and rounded to E4M3 before they multiply V; the factor cancels in
+ *    the normalisation.  Rounding P to E4M3 (relative error up to 2^-4) is
+ *    the dominant error of this path.
+ *  - q_descale, k_descale, v_descale: DEVICE pointers to float32 [B * H],
+ *    4-byte aligned, finite and positive (not checked on the host).
+ *  - Everything else as for fa_fwd. */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale,
+               const float* k_descale, const float* v_descale, void* o, float* lse,
+               int B, int H, int N, int d, float scale, int mask_kind,
+               const int32_t* kv_lens, void* stream);
+
 /* bfloat16 backward: the gradients of the attention above with respect to
  * q, k and v, given the upstream gradient dout = dL/dO.  With P the softmax
  * probabilities of the forward ("FlashAttention算法详解：从IO瓶颈到Triton实现",

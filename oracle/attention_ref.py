@@ -66,11 +66,15 @@ def _kv_len(mask_kind: int, kv_lens, b: int, N: int) -> int:
     return N
 
 
-def _head_ref(qh, kh, vh, scale, causal, n_vis, rows, row_block):
-    """Definition of O and LSE for one (b, h) over the query rows ``rows``."""
+def _head_ref(qh, kh, vh, scale, causal, n_vis, rows, row_block, mags=None):
+    """Definition of O and LSE for one (b, h) over the query rows ``rows``.
+    With ``mags`` (a dict), also P |V| and (sum over visible keys of |V|) / l."""
     d = vh.shape[1]
     out = np.zeros((len(rows), d), dtype=np.float64)
     lse = np.full(len(rows), -np.inf, dtype=np.float64)
+    if mags is not None:
+        mags["pv"] = np.zeros((len(rows), d))
+        mags["v_over_l"] = np.zeros((len(rows), d))
     for start in range(0, len(rows), row_block):
         rr = rows[start:start + row_block]
         kmax = min(n_vis, int(rr.max()) + 1) if causal else n_vis
@@ -88,12 +92,16 @@ def _head_ref(qh, kh, vh, scale, causal, n_vis, rows, row_block):
         idx = start + np.nonzero(ok)[0]
         out[idx] = (p @ vh[:kmax]) / l[:, None]  # P V with P = p / l
         lse[idx] = m[ok] + np.log(l)
+        if mags is not None:
+            av = np.abs(vh[:kmax])
+            mags["pv"][idx] = (p @ av) / l[:, None]
+            mags["v_over_l"][idx] = (np.isfinite(s[ok]).astype(np.float64) @ av) / l[:, None]
     return out, lse
 
 
 def attention_ref(q, k, v, scale, mask_kind=MASK_NONE, kv_lens=None,
                   rows: Optional[Sequence[int]] = None, heads=None,
-                  row_block: int = 512, workers: int = 1):
+                  row_block: int = 512, workers: int = 1, magnitudes: bool = False):
     """fp64 O and LSE of exact attention.
 
     q, k, v: float64 arrays ``[B, H, N, d]`` (callers widen the generated
@@ -101,6 +109,12 @@ def attention_ref(q, k, v, scale, mask_kind=MASK_NONE, kv_lens=None,
     compute (default: all).  ``heads``: optional list of (b, h) pairs
     (default: all).  Returns ``O [B, H, R, d]`` and ``LSE [B, H, R]``; rows
     of heads not requested are left NaN.
+
+    ``magnitudes=True`` appends a dict with, per output element, ``pv`` =
+    (P |V|)_rt and ``v_over_l`` = (sum over the visible keys of |v_ct|) / l_r,
+    with l_r the max-subtracted row sum (at least 1).  They bound how far
+    per-probability rounding errors (relative and absolute) can move O; they
+    are for tolerances only.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -118,12 +132,18 @@ def attention_ref(q, k, v, scale, mask_kind=MASK_NONE, kv_lens=None,
     units = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
     O = np.full((B, H, len(rows), d), np.nan)
     L = np.full((B, H, len(rows)), np.nan)
+    M = ({"pv": np.full(O.shape, np.nan), "v_over_l": np.full(O.shape, np.nan)}
+         if magnitudes else None)
 
     def run(unit):
         b, h = unit
         n_vis = _kv_len(mask_kind, kv_lens, b, N)
+        mags = {} if magnitudes else None
         O[b, h], L[b, h] = _head_ref(q[b, h], k[b, h], v[b, h], scale, causal,
-                                     n_vis, rows, row_block)
+                                     n_vis, rows, row_block, mags)
+        if magnitudes:
+            for name in M:
+                M[name][b, h] = mags[name]
 
     if workers <= 1 or len(units) == 1:
         for u in units:
@@ -134,6 +154,8 @@ def attention_ref(q, k, v, scale, mask_kind=MASK_NONE, kv_lens=None,
         from threadpoolctl import threadpool_limits
         with threadpool_limits(1), ThreadPoolExecutor(workers) as ex:
             list(ex.map(run, units))
+    if magnitudes:
+        return O, L, M
     return O, L
 
 

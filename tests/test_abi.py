@@ -26,7 +26,7 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared() == ["fa_bwd", "fa_fwd", "fa_fwd_f32", "fa_strerror"]
+    assert _declared() == ["fa_bwd", "fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_strerror"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -93,6 +93,34 @@ def test_backward_invalid_arguments_are_rejected_before_launch(lib):
     assert _bwd(lib, scale=float("-inf")) == bad
     assert _bwd(lib, B=1 << 20, H=1 << 10, N=1 << 20) == bad
     assert _bwd(lib, d=32) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_fp8_invalid_arguments_are_rejected_before_launch(lib):
+    import exact_attention_92_amd as fa
+    bad = fa.FA_ERR_INVALID_ARG
+    good = [0x1000 * (i + 1) for i in range(8)]
+
+    def call(ptrs=good, B=1, H=1, N=16, d=64, scale=0.125, mask=0, kv=None):
+        return lib.fa_fwd_fp8(*[ctypes.c_void_p(p) if p is not None else None for p in ptrs],
+                              B, H, N, d, ctypes.c_float(scale), mask,
+                              ctypes.c_void_p(kv) if kv else None, None)
+    for i in range(8):
+        p = list(good)
+        p[i] = None
+        assert call(p) == bad, i
+    for i in (0, 1, 2, 6, 7):          # tensors: 16-byte alignment
+        p = list(good)
+        p[i] = good[i] + 8
+        assert call(p) == bad, i
+    for i in (3, 4, 5):                # scales: 4-byte alignment
+        p = list(good)
+        p[i] = good[i] + 2
+        assert call(p) == bad, i
+    assert call(N=0) == bad
+    assert call(mask=4) == bad
+    assert call(mask=fa.FA_MASK_KEY_PADDING) == bad
+    assert call(scale=float("nan")) == bad
+    assert call(d=256) == fa.FA_ERR_UNSUPPORTED
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

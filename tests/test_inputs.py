@@ -71,3 +71,47 @@ def test_grad_out_stream_leaves_forward_inputs_unchanged():
     assert not np.array_equal(y["do"], y["q"])
     f = make_grad_out(1, 2, 8, 4, "f32", 3)
     assert f.dtype == np.float32 and abs(float(f.mean())) < 1.0
+
+
+def test_fp8_e4m3_encoding_matches_torch():
+    """Every float32 that rounds to each code, the ties between codes, the
+    subnormals and the clamp at 448 agree with torch's float8_e4m3fn."""
+    torch = pytest.importorskip("torch")
+    from fa_inputs import FP8_MAX, f32_to_fp8_e4m3, fp8_e4m3_to_f64
+    codes = np.arange(256, dtype=np.uint8)
+    vals = fp8_e4m3_to_f64(codes)
+    fin = np.isfinite(vals)
+    assert np.nanmax(vals) == FP8_MAX and np.isnan(vals[0x7F]) and np.isnan(vals[0xFF])
+    # Round trip of every finite code (negative zero keeps its sign bit).
+    assert np.array_equal(f32_to_fp8_e4m3(vals[fin]), codes[fin])
+    pos = np.sort(vals[(vals >= 0) & fin])
+    mids = (pos[1:] + pos[:-1]) / 2
+    g = np.random.default_rng(0)
+    x = np.concatenate([pos, mids, -mids, np.nextafter(mids.astype(np.float32), 0),
+                        np.nextafter(mids.astype(np.float32), 1000),
+                        g.standard_normal(20000) * 40, g.standard_normal(2000) * 1e-3,
+                        [447.9, 448.0, 460.0, 463.99, -448.0]]).astype(np.float32)
+    want = torch.from_numpy(np.clip(x, -FP8_MAX, FP8_MAX)).to(torch.float8_e4m3fn)
+    assert np.array_equal(f32_to_fp8_e4m3(x), want.view(torch.uint8).numpy())
+    assert np.array_equal(fp8_e4m3_to_f64(want.view(torch.uint8).numpy()),
+                          want.to(torch.float64).numpy())
+
+
+def test_fp8_per_head_quantization_recipe():
+    from fa_inputs import FP8_WORKLOADS, inputs_f64, make_inputs, make_raw
+    wl = FP8_WORKLOADS["fp8_b2h32_n4096_d128_causal"]
+    x = make_raw(2, 3, 64, 64, "fp8", seed=3, q_mult=2.0)
+    ref = make_raw(2, 3, 64, 64, "f32", seed=3, q_mult=2.0)
+    q, k, v = inputs_f64(x)
+    for name, deq in zip("qkv", (q, k, v)):
+        ds = x[name + "_descale"]
+        assert ds.shape == (2, 3) and ds.dtype == np.float32
+        amax = np.abs(ref[name]).max(axis=(2, 3))
+        assert np.allclose(ds, amax / 448.0, rtol=1e-7)
+        # Each head uses its full range, and the relative error is within the
+        # E4M3 rounding bound (half a step: 2^-4 relative for normal values).
+        assert np.max(np.abs(x[name]) & 0x7F) == 0x7E
+        err = np.abs(deq - ref[name])
+        scale = ds[:, :, None, None].astype(np.float64)
+        assert np.all(err <= np.maximum(2.0 ** -4 * np.abs(ref[name]), 2.0 ** -10 * scale) * 1.0001)
+    assert wl.dtype == "fp8" and make_inputs(wl)["q"].dtype == np.uint8

@@ -250,6 +250,25 @@ def test_scale_is_the_float32_value():
     assert np.array_equal(O1, O2)
 
 
+@pytest.mark.parametrize("mask", MASKS)
+def test_forward_magnitudes(mask):
+    """P |V| bounds |O| (equal when V >= 0); (sum_J |v|) / l bounds P |V|
+    (P_rc = p_rc / l with p_rc <= 1); row-sum identity against probabilities_ref."""
+    q, k, v = _rand(2, 2, 30, 6, seed=33)
+    kv = np.array([0, 17], dtype=np.int32)
+    O, L = attention_ref(q, k, v, 0.4, mask, kv)
+    O2, L2, M = attention_ref(q, k, v, 0.4, mask, kv, magnitudes=True, row_block=7)
+    assert np.array_equal(O, O2) or np.max(np.abs(O - O2)) <= 1e-13
+    assert np.all(M["pv"] >= np.abs(O) - 1e-13)
+    assert np.all(M["v_over_l"] >= M["pv"] - 1e-13)
+    O3, _, M3 = attention_ref(q, k, np.abs(v), 0.4, mask, kv, magnitudes=True)
+    assert np.max(np.abs(M3["pv"] - O3)) <= 1e-13
+    for b in range(2):
+        for h in range(2):
+            P = probabilities_ref(q, k, 0.4, mask, kv, b, h)
+            assert np.max(np.abs(M["pv"][b, h] - P @ np.abs(v[b, h]))) <= 1e-12
+
+
 def test_rejects_bad_arguments():
     q, k, v = _rand(1, 1, 4, 2, seed=20)
     with pytest.raises(ValueError):
