@@ -20,10 +20,11 @@
 //    that same order, so the rounded probabilities are directly the B
 //    operand of O^T = V^T P^T (two 16-byte LDS reads per operand).
 //  * The row max is exact (updated every block), so every probability is at
-//    most 1; P is multiplied by 448 (the largest E4M3 value) before rounding,
-//    which keeps values down to ~4e-6 representable.  The factor and the
-//    V scale are divided out once in the epilogue; the row sum is the fp32
-//    sum of the unrounded probabilities (it also gives LSE).
+//    most 1; P is scaled by 448 (the largest E4M3 value) before rounding --
+//    folded into the exponent -- which keeps values down to ~4e-6
+//    representable.  The factor and the V scale are divided out once in the
+//    epilogue; the row sum is the fp32 sum of the unrounded scaled
+//    probabilities (it also gives LSE).
 //  * The per-head Q and K scales fold into the exp2 constant, the V scale
 //    into the final division.
 #include <hip/hip_runtime.h>
@@ -39,7 +40,8 @@ using namespace fa92;
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
-constexpr float kP8Scale = 448.f;   // largest finite E4M3 value
+// log2(448); 448 is the largest finite E4M3 value.
+constexpr float kLog2P8Scale = 8.807354922057604f;
 
 // D = A B + C, 32x32 tile, 64-deep E4M3 contraction, fp32 accumulation.
 // Lane l supplies A row / B column l%32, 32 contraction elements per lane
@@ -254,9 +256,10 @@ void fa_fwd_fp8_kernel(P8Params p) {
         l_run *= alpha;
         m_run = m_new;
       }
-      const float base = (m_run == -INFINITY) ? 0.f : m_run;
-      // p = 2^(s c - m) <= 1; the P^T operand holds 448 p rounded to E4M3,
-      // byte 16kt + r of the lane's 32 = register r of tile kt.
+      // e = 448 p = 2^(s c - m + log2 448) <= 448 (p <= 1); the P^T operand
+      // holds e rounded to E4M3, byte 16kt + r of the lane's 32 = register r
+      // of tile kt.  The row sum accumulates e, i.e. 448 times the sum of p.
+      const float base = ((m_run == -INFINITY) ? 0.f : m_run) - kLog2P8Scale;
       i32x8_t pb;
       float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
@@ -269,8 +272,7 @@ void fa_fwd_fp8_kernel(P8Params p) {
             e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][4 * g + i], c, -base));
           rs0 += e[0] + e[1];
           rs1 += e[2] + e[3];
-          pb[4 * kt + g] = (int)pack_fp8x4(e[0] * kP8Scale, e[1] * kP8Scale, e[2] * kP8Scale,
-                                           e[3] * kP8Scale);
+          pb[4 * kt + g] = (int)pack_fp8x4(e[0], e[1], e[2], e[3]);
         }
       l_run += rs0 + rs1;
       // O^T += V_j^T P^T: A operand = V^T row 32dt + n, positions 32hf + 0..31.
@@ -284,12 +286,12 @@ void fa_fwd_fp8_kernel(P8Params p) {
     __syncthreads();
   }
 
-  // Epilogue: O = acc * v_descale / (448 l), rounded to bf16 once;
-  // LSE = (m + log2 l) ln 2.
+  // Epilogue (l_run holds 448 times the row sum): O = acc * v_descale / l_run,
+  // rounded to bf16 once; LSE = (m + log2(l_run) - log2 448) ln 2.
   uint16_t* __restrict__ Oh = (uint16_t*)p.o + hoff;
   float* __restrict__ Lh = p.lse + (size_t)bh * N;
   const float lt = pair_sum(l_run);
-  const float inv = lt > 0.f ? p.v_descale[bh] / (kP8Scale * lt) : 0.f;
+  const float inv = lt > 0.f ? p.v_descale[bh] / lt : 0.f;
   if (qrow < N) {
     uint16_t* orow = Oh + (size_t)qrow * D;
 #pragma unroll
@@ -300,7 +302,8 @@ void fa_fwd_fp8_kernel(P8Params p) {
                      pack_bf16(acc[dt][4 * a + 2] * inv, acc[dt][4 * a + 3] * inv)};
         *(u32x2_t*)(orow + 32 * dt + 8 * a + 4 * hf) = x;
       }
-    if (hf == 0) Lh[qrow] = lt > 0.f ? (m_run + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+    if (hf == 0)
+      Lh[qrow] = lt > 0.f ? (m_run + __builtin_amdgcn_logf(lt) - kLog2P8Scale) * kLn2 : -INFINITY;
   }
 }
 
