@@ -21,6 +21,15 @@ Recipe (identical for every workload):
   and tensor: descale = max|x| / 448 over that head's [N, d] values, code =
   nearest E4M3 value of x / descale (ties to the even code).  The
   dequantized value is code_value * descale.
+* Paged decode (one query token per request against a paged KV cache):
+  ``SeedSequence(seed).spawn(5)`` streams for q, the K pool, the V pool,
+  the request lengths and the block placement.  Lengths are uniform over the
+  inclusive ``len_range``; request b needs ceil(n_b / block_size) blocks;
+  the pool holds exactly those blocks plus ``spare`` unused ones, placed by
+  a random permutation (so a request's blocks are scattered through the
+  pool); table entries past a request's last block hold -1.  q and both
+  pools are float32 N(0,1) rounded to bf16, pools shaped
+  [num_blocks, H, block_size, d].
 * The backward pass's upstream gradient dO (same shape as O) comes from a
   fifth stream, ``SeedSequence(seed).spawn(5)[4]`` (the first four children
   are the ones above, so the forward inputs do not change): float32
@@ -99,6 +108,30 @@ FP8_WORKLOADS = {
         "fp8_b2h32_n4096_d128_causal", 2, 32, 4096, 128, "fp8", MASK_CAUSAL, seed=3,
         q_mult=2.0, note="fp8 E4M3 Q, K, V with per-head scales; causal"),
 }
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """One paged-KV decode workload (one query token per request)."""
+
+    name: str
+    B: int
+    H: int
+    d: int
+    block_size: int
+    len_range: Tuple[int, int]
+    seed: int
+    spare: int = 16
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / np.sqrt(self.d)))
+
+
+DECODE_WORKLOADS = {
+    "decode_b32h32_d128_bs64_len1k8k": DecodeWorkload(
+        "decode_b32h32_d128_bs64_len1k8k", 32, 32, 128, 64, (1024, 8192), seed=6),
+}
+
 
 # The workload the throughput figure is quoted on.
 BENCH_WORKLOAD = "bf16_b2h32_n4096_d128_causal"
@@ -219,6 +252,37 @@ def make_grad_out(B: int, H: int, N: int, d: int, dtype: str, seed: int):
     g = _streams(seed, 5)[4]
     do = g.standard_normal((B, H, N, d), dtype=np.float32)
     return f32_to_bf16_bits(do) if dtype == "bf16" else do
+
+
+def make_paged_decode(B: int, H: int, d: int, block_size: int, len_range, seed: int,
+                      spare: int = 16):
+    """Draw a paged-KV decode batch (see the recipe above).  Returns a dict:
+    ``q`` [B, H, d], ``k_pool``/``v_pool`` [num_blocks, H, block_size, d]
+    (bf16 bits), ``block_tables`` int32 [B, max_blocks], ``seq_lens`` int32 [B]."""
+    gq, gk, gv, gl, gp = _streams(seed, 5)
+    lo, hi = len_range
+    lens = gl.integers(lo, hi, size=B, endpoint=True).astype(np.int32)
+    nblk = (lens.astype(np.int64) + block_size - 1) // block_size
+    max_blocks = max(1, int(nblk.max()))
+    num_blocks = int(nblk.sum()) + spare
+    perm = gp.permutation(num_blocks).astype(np.int32)
+    tables = np.full((B, max_blocks), -1, dtype=np.int32)
+    at = 0
+    for b in range(B):
+        tables[b, :nblk[b]] = perm[at:at + nblk[b]]
+        at += int(nblk[b])
+    shape = (num_blocks, H, block_size, d)
+
+    def pool(g):
+        out = np.empty(shape, dtype=np.uint16)
+        for i in range(0, num_blocks, 256):          # in chunks: bounded float32 staging
+            j = min(num_blocks, i + 256)
+            out[i:j] = f32_to_bf16_bits(g.standard_normal((j - i,) + shape[1:], dtype=np.float32))
+        return out
+
+    q = f32_to_bf16_bits(gq.standard_normal((B, H, d), dtype=np.float32))
+    return {"q": q, "k_pool": pool(gk), "v_pool": pool(gv), "block_tables": tables,
+            "seq_lens": lens}
 
 
 def make_inputs(wl: Workload):
