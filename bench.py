@@ -13,6 +13,11 @@ timed on the host as a reported baseline.
 ``--pass bwd`` times one fa_bwd call per step instead (the forward runs once,
 untimed, to produce O and LSE); FLOPs are counted as the five products of the
 gradient, 2.5x the forward's.
+
+``--pass decode`` times one fa_decode_paged call per step (one query token
+per request against a paged KV cache); it is bandwidth-bound, so the figure
+is GB/s of algorithmic bytes (every cached K and V row once, q, O and LSE)
+against the 8 TB/s HBM peak.
 """
 import argparse
 import hashlib
@@ -33,10 +38,14 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "fp8": 5000.0}   # MI355X dense MFM
 CSRC = os.path.join(ROOT, "exact_attention_92_amd", "csrc")
 # Sources each pass's kernels are built from (the PMC summaries record their hash).
 KERNEL_SRCS = {"fwd": ["fa_fwd.hip"], "bwd": ["fa_bwd.hip", "fa_device.h"],
-               "fp8": ["fa_fwd_fp8.hip", "fa_device.h"]}
+               "fp8": ["fa_fwd_fp8.hip", "fa_device.h"],
+               "decode": ["fa_decode.hip", "fa_device.h"]}
 PMC_SUMMARY = {"fwd": os.path.join(ROOT, "profiles", "fa_fwd_bf16_b2h32_n4096_d128_causal_pmc.md"),
                "bwd": os.path.join(ROOT, "profiles", "fa_bwd_bf16_b2h32_n4096_d128_causal_pmc.md"),
-               "fp8": os.path.join(ROOT, "profiles", "fa_fwd_fp8_b2h32_n4096_d128_causal_pmc.md")}
+               "fp8": os.path.join(ROOT, "profiles", "fa_fwd_fp8_b2h32_n4096_d128_causal_pmc.md"),
+               "decode": os.path.join(ROOT, "profiles",
+                                      "fa_decode_paged_b32h32_d128_bs64_len1k8k_pmc.md")}
+HBM_PEAK_GBS = 8000.0
 
 
 def kernel_source_hash(which="fwd"):
@@ -102,6 +111,90 @@ def cpu_baseline_bwd(x, wl, g):
                       f"{cores} worker threads with single-threaded BLAS"}, parity
 
 
+def decode_bench(args):
+    """One fa_decode_paged call per step over a paged-KV decode batch."""
+    import torch
+
+    import exact_attention_92_amd as fa
+    from fa_inputs import DECODE_WORKLOADS, bf16_bits_to_f32, make_paged_decode
+    name = args.workload or "decode_b32h32_d128_bs64_len1k8k"
+    wl = DECODE_WORKLOADS[name]
+    x = make_paged_decode(wl.B, wl.H, wl.d, wl.block_size, wl.len_range, wl.seed, wl.spare)
+    dev = torch.device("cuda:0")
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    q, kp, vp = bf(x["q"]), bf(x["k_pool"]), bf(x["v_pool"])
+    tab = torch.from_numpy(x["block_tables"]).to(dev)
+    lens = torch.from_numpy(x["seq_lens"]).to(dev)
+    o = torch.empty((wl.B, wl.H, wl.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((wl.B, wl.H), dtype=torch.float32, device=dev)
+    need = fa.fa_decode_paged_workspace_bytes(wl.B, wl.H, wl.d, wl.block_size, tab.shape[1])
+    ws = torch.empty(((need + 3) // 4,), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        fa.fa_decode_paged(q, kp, vp, tab, lens, o, lse, ws, wl.scale, stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    launch_ms = [a.elapsed_time(b) for a, b in evs]
+    avg_ms = float(np.mean(launch_ms))
+    ntok = int(x["seq_lens"].astype(np.int64).sum())
+    nbytes = ntok * wl.H * wl.d * 2 * 2 + 2 * wl.B * wl.H * wl.d * 2 + wl.B * wl.H * 4
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (avg_ms * 1e-3) / 1e9
+    rec = {
+        "metric": f"paged-KV decode GB/s ({wl.name})",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "pct_of_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "d": wl.d,
+                   "block_size": wl.block_size, "len_range": list(wl.len_range),
+                   "cached_tokens": ntok, "bytes_per_step": nbytes,
+                   "device": torch.cuda.get_device_name(dev)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("decode"),
+                     "kernel": "fa_decode_split_kernel + fa_decode_combine_kernel (one call)",
+                     "avg_launch_us": round(avg_ms * 1e3, 2),
+                     "min_launch_us": round(min(launch_ms) * 1e3, 2)},
+        "cpu_baseline": None, "pass": "decode",
+    }
+    if not args.no_cpu_baseline:
+        from oracle.paged_decode_ref import paged_decode_ref
+        f = bf16_bits_to_f32
+        kp32, vp32 = f(x["k_pool"]), f(x["v_pool"])
+        t0 = time.perf_counter()
+        Or, Lr = paged_decode_ref(f(x["q"]), kp32, vp32, x["block_tables"], x["seq_lens"],
+                                  wl.scale)
+        dt = time.perf_counter() - t0
+        og = o.float().cpu().numpy().astype(np.float64)
+        rec["cpu_baseline"] = {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle", "seconds": round(dt, 3),
+                               "sample": f"the whole batch ({wl.B} requests x {wl.H} heads), "
+                                         "fp64 NumPy, one thread"}
+        rec["parity_vs_oracle"] = {"o_max_abs": float(np.abs(og - Or).max()),
+                                   "o_rel_frobenius": float(np.linalg.norm(og - Or) /
+                                                            np.linalg.norm(Or))}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -109,7 +202,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd", "decode"), default="fwd")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="first run 3 plain device copies of this many MiB (a known-size "
                          "reference for HBM byte counters)")
@@ -118,6 +211,10 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the attention forward here runs on a single MI355X).", file=sys.stderr)
         sys.exit(2)
+
+    if args.which == "decode":
+        decode_bench(args)
+        return
 
     import torch
 

@@ -1,8 +1,8 @@
 """Exact attention on MI355X (gfx950): Python binding of libfa92.so.
 
 The binding only marshals arguments: every step of the forward and backward
-passes runs in the HIP kernels of ``csrc/fa_fwd.hip``, ``csrc/fa_fwd_fp8.hip`` and
-``csrc/fa_bwd.hip``.  PyTorch supplies device memory and
+passes runs in the HIP kernels of ``csrc/fa_fwd.hip``, ``csrc/fa_fwd_fp8.hip``,
+``csrc/fa_bwd.hip`` and ``csrc/fa_decode.hip``.  PyTorch supplies device memory and
 the stream.  There is no CPU or PyTorch fallback: if the library is missing
 or the GPU is absent, the calls raise.
 
@@ -14,6 +14,9 @@ Names follow the C ABI of ``include/fa_api.h``:
 * ``fa_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, o, lse, scale,
   mask_kind=0, kv_lens=None, stream=None)`` -- E4M3 codes (uint8 tensors)
   with per-(batch, head) float32 scales; o is bf16
+* ``fa_decode_paged(q, k_pool, v_pool, block_tables, seq_lens, o, lse,
+  workspace, scale, num_blocks=None, stream=None)`` and
+  ``fa_decode_paged_workspace_bytes(B, H, d, block_size, max_blocks)``
 * ``fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, dp_rowsum, scale, mask_kind=0,
   kv_lens=None, stream=None)`` -- bf16 gradients
 * ``fa_strerror(status)``
@@ -36,7 +39,8 @@ FA_ERR_UNSUPPORTED = -2
 FA_ERR_HIP = -3
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa92.so")
-EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_bwd", "fa_strerror")
+EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_bwd", "fa_decode_paged",
+           "fa_decode_paged_workspace_bytes", "fa_strerror")
 
 _lib = None
 
@@ -64,6 +68,10 @@ def load_library():
         fn.restype = i32
     lib.fa_fwd_fp8.argtypes = [vp] * 8 + [i32, i32, i32, i32, f32, i32, vp, vp]
     lib.fa_fwd_fp8.restype = i32
+    lib.fa_decode_paged.argtypes = [vp] * 8 + [i32] * 6 + [f32, vp]
+    lib.fa_decode_paged.restype = i32
+    lib.fa_decode_paged_workspace_bytes.argtypes = [i32] * 5
+    lib.fa_decode_paged_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_bwd.argtypes = [vp] * 10 + [i32, i32, i32, i32, f32, i32, vp, vp]
     lib.fa_bwd.restype = i32
     lib.fa_strerror.argtypes = [i32]
@@ -156,6 +164,43 @@ def fa_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, o, lse, scale, mask_kin
                         _ptr(v_descale), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
                         int(mask_kind), _ptr(kv_lens),
                         ctypes.c_void_p(_stream_handle(stream, q.device)))
+    if st != FA_OK:
+        raise FaError(st, fa_strerror(st))
+
+
+def fa_decode_paged_workspace_bytes(B, H, d, block_size, max_blocks):
+    return int(load_library().fa_decode_paged_workspace_bytes(B, H, d, block_size, max_blocks))
+
+
+def fa_decode_paged(q, k_pool, v_pool, block_tables, seq_lens, o, lse, workspace, scale,
+                    stream=None):
+    """Decode over a paged KV cache: q bf16 [B, H, d]; pools bf16
+    [num_blocks, H, block_size, d]; block_tables int32 [B, max_blocks];
+    seq_lens int32 [B]; writes o (bf16 [B, H, d]) and lse (float32 [B, H])."""
+    import torch
+    lib = load_library()
+    B, H, d = q.shape
+    nblk, Hp, bs, dp = k_pool.shape
+    for nm, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("o", o)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{nm} must be a contiguous bf16 device tensor")
+    if v_pool.shape != k_pool.shape or Hp != H or dp != d or tuple(o.shape) != (B, H, d):
+        raise ValueError("pools must be [num_blocks, H, block_size, d] and o [B, H, d]")
+    for nm, t, shp in (("block_tables", block_tables, None), ("seq_lens", seq_lens, (B,))):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{nm} must be a contiguous int32 device tensor")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or tuple(seq_lens.shape) != (B,):
+        raise ValueError("block_tables must be [B, max_blocks] and seq_lens [B]")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H) or not lse.is_cuda:
+        raise ValueError("lse must be a float32 device tensor [B, H]")
+    need = fa_decode_paged_workspace_bytes(B, H, d, bs, block_tables.shape[1])
+    if workspace.dtype != torch.float32 or not workspace.is_cuda \
+            or workspace.numel() * 4 < need:
+        raise ValueError(f"workspace must be a float32 device tensor of >= {need} bytes")
+    st = lib.fa_decode_paged(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+                             _ptr(seq_lens), _ptr(o), _ptr(lse), _ptr(workspace), B, H, d, bs,
+                             block_tables.shape[1], nblk, float(scale),
+                             ctypes.c_void_p(_stream_handle(stream, q.device)))
     if st != FA_OK:
         raise FaError(st, fa_strerror(st))
 

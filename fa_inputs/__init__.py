@@ -255,13 +255,15 @@ def make_grad_out(B: int, H: int, N: int, d: int, dtype: str, seed: int):
 
 
 def make_paged_decode(B: int, H: int, d: int, block_size: int, len_range, seed: int,
-                      spare: int = 16):
+                      spare: int = 16, lens=None):
     """Draw a paged-KV decode batch (see the recipe above).  Returns a dict:
     ``q`` [B, H, d], ``k_pool``/``v_pool`` [num_blocks, H, block_size, d]
-    (bf16 bits), ``block_tables`` int32 [B, max_blocks], ``seq_lens`` int32 [B]."""
+    (bf16 bits), ``block_tables`` int32 [B, max_blocks], ``seq_lens`` int32 [B].
+    ``lens`` (optional) replaces the drawn lengths."""
     gq, gk, gv, gl, gp = _streams(seed, 5)
     lo, hi = len_range
-    lens = gl.integers(lo, hi, size=B, endpoint=True).astype(np.int32)
+    drawn = gl.integers(lo, hi, size=B, endpoint=True).astype(np.int32)
+    lens = drawn if lens is None else np.asarray(lens, dtype=np.int32)
     nblk = (lens.astype(np.int64) + block_size - 1) // block_size
     max_blocks = max(1, int(nblk.max()))
     num_blocks = int(nblk.sum()) + spare

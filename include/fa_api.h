@@ -1,6 +1,6 @@
 /*
  * fa_api.h -- C ABI of the exact attention library (libfa92.so): the
- * forward pass and the backward pass.
+ * forward pass (bf16, fp32, fp8), the backward pass and paged decode.
  *
  * What the library computes, for every batch entry b and head h:
  *
@@ -55,6 +55,7 @@
 #ifndef FA_API_H
 #define FA_API_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -111,6 +112,37 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, const float* q_desca
                const float* k_descale, const float* v_descale, void* o, float* lse,
                int B, int H, int N, int d, float scale, int mask_kind,
                const int32_t* kv_lens, void* stream);
+
+/* Decode over a paged KV cache ("FlashAttention 完整解析" §7, PageAttention's
+ * block table): for each request b and head h, the one query vector
+ * q[b, h, :] attends to the request's n_b = seq_lens[b] cached tokens,
+ * which are stored in a pool of fixed-size blocks:
+ *
+ *     k_t = k_pool[block_tables[b, t / block_size], h, t % block_size, :]
+ *     O[b, h] = softmax(scale * q . k_t over t < n_b) V,   LSE[b, h]
+ *
+ * (v_t likewise), i.e. the newest token's row of causal attention.
+ *  - q: DEVICE bf16 [B, H, d]; k_pool, v_pool: DEVICE bf16
+ *    [num_blocks, H, block_size, d]; all 16-byte aligned, read only.
+ *  - block_tables: DEVICE int32 [B, max_blocks_per_seq]; entries past a
+ *    request's last block are never read; an entry outside [0, num_blocks)
+ *    reads as zeros (memory-safe; the result is then meaningless).
+ *  - seq_lens: DEVICE int32 [B], clamped on the device to
+ *    [0, max_blocks_per_seq * block_size]; n_b = 0 gives O = 0, LSE = -inf.
+ *  - o: DEVICE bf16 [B, H, d]; lse: DEVICE float32 [B, H].
+ *  - workspace: DEVICE float32 scratch of fa_decode_paged_workspace_bytes()
+ *    bytes, caller-owned; it holds per-chunk partial results between the two
+ *    kernels the call enqueues (calls that share a workspace must not
+ *    overlap).
+ *  - d is 64 or 128; block_size a multiple of 8 (8 .. 65536); any finite
+ *    scale; B, H <= 65535.  Errors as for fa_fwd.  The library allocates
+ *    nothing. */
+size_t fa_decode_paged_workspace_bytes(int B, int H, int d, int block_size,
+                                       int max_blocks_per_seq);
+int fa_decode_paged(const void* q, const void* k_pool, const void* v_pool,
+                    const int32_t* block_tables, const int32_t* seq_lens, void* o,
+                    float* lse, float* workspace, int B, int H, int d, int block_size,
+                    int max_blocks_per_seq, int num_blocks, float scale, void* stream);
 
 /* bfloat16 backward: the gradients of the attention above with respect to
  * q, k and v, given the upstream gradient dout = dL/dO.  With P the softmax

@@ -26,7 +26,8 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared() == ["fa_bwd", "fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_strerror"]
+    assert _declared() == ["fa_bwd", "fa_decode_paged", "fa_decode_paged_workspace_bytes", "fa_fwd",
+                           "fa_fwd_f32", "fa_fwd_fp8", "fa_strerror"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -121,6 +122,28 @@ def test_fp8_invalid_arguments_are_rejected_before_launch(lib):
     assert call(mask=fa.FA_MASK_KEY_PADDING) == bad
     assert call(scale=float("nan")) == bad
     assert call(d=256) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_decode_invalid_arguments_are_rejected_before_launch(lib):
+    import exact_attention_92_amd as fa
+    bad = fa.FA_ERR_INVALID_ARG
+    good = [0x1000 * (i + 1) for i in range(8)]
+
+    def call(ptrs=good, B=2, H=2, d=128, bs=64, mb=4, nb=8, scale=0.1):
+        return lib.fa_decode_paged(*[ctypes.c_void_p(p) if p is not None else None for p in ptrs],
+                                   B, H, d, bs, mb, nb, ctypes.c_float(scale), None)
+    for i in range(8):
+        p = list(good)
+        p[i] = None
+        assert call(p) == bad, i
+        p[i] = good[i] + (8 if i in (0, 1, 2, 5) else 2)
+        assert call(p) == bad, i
+    assert call(B=0) == bad and call(mb=0) == bad and call(nb=0) == bad
+    assert call(bs=12) == bad and call(bs=4) == bad
+    assert call(scale=float("inf")) == bad
+    assert call(d=96) == fa.FA_ERR_UNSUPPORTED
+    assert lib.fa_decode_paged_workspace_bytes(2, 2, 128, 64, 4) == 2 * 2 * 1 * 130 * 4
+    assert lib.fa_decode_paged_workspace_bytes(2, 2, 96, 64, 4) == 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
