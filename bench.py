@@ -212,15 +212,7 @@ def main():
               "(the attention forward here runs on a single MI355X).", file=sys.stderr)
         sys.exit(2)
 
-    if args.which == "decode":
-        decode_bench(args)
-        return
-
     import torch
-
-    import exact_attention_92_amd as fa
-    from fa_inputs import (BENCH_WORKLOAD, FP8_WORKLOADS, WORKLOADS, bf16_bits_to_f32,
-                           make_bwd_inputs, make_inputs)
 
     if args.copy_mib > 0:
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device="cuda:0")
@@ -229,6 +221,14 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.which == "decode":
+        decode_bench(args)
+        return
+
+    import exact_attention_92_amd as fa
+    from fa_inputs import (BENCH_WORKLOAD, FP8_WORKLOADS, WORKLOADS, bf16_bits_to_f32,
+                           make_bwd_inputs, make_inputs)
 
     wl = {**WORKLOADS, **FP8_WORKLOADS}[args.workload or BENCH_WORKLOAD]
     bwd = args.which == "bwd"
