@@ -294,3 +294,60 @@ def brute_ref(q, k, v, scale, mask_kind=MASK_NONE, kv_lens=None):
                     O[b, h, r, t] = math.fsum(e[c] * float(v[b, h, c, t]) for c in J) / den
                 L[b, h, r] = mx + math.log(den)
     return O, L
+
+
+# ---------------------------------------------------------------------------
+# General masks: N_q != N_k, sliding window.
+# ---------------------------------------------------------------------------
+
+def visible_general(Nq: int, Nk: int, causal: bool, window_left: int, n_vis: int):
+    """Boolean [Nq, Nk] visibility for the general forward.
+
+    Query r sits at key position a_r = r + (Nk - Nq) (the queries are the last
+    Nq positions of the key sequence).  Key c is visible to query r iff
+    c < n_vis, and c <= a_r when causal, and c >= a_r - window_left when
+    window_left >= 0 (a window of window_left keys before the query's own
+    position).
+    """
+    r = np.arange(Nq)[:, None] + (Nk - Nq)
+    c = np.arange(Nk)[None, :]
+    vis = c < n_vis
+    if causal:
+        vis = vis & (c <= r)
+    if window_left >= 0:
+        vis = vis & (c >= r - window_left)
+    return np.broadcast_to(vis, (Nq, Nk))
+
+
+def attention_general_ref(q, k, v, scale, mask_kind=MASK_NONE, window_left: int = -1,
+                          kv_lens=None):
+    """fp64 O [B, H, Nq, d] and LSE [B, H, Nq] with N_q != N_k allowed and an
+    optional sliding window (see visible_general); the same definition as
+    attention_ref otherwise (max-subtracted softmax over the visible keys;
+    a row with no visible key has O = 0, LSE = -inf)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, d) or v.shape != k.shape:
+        raise ValueError("k, v must be [B, H, Nk, d] with q's B, H, d")
+    if mask_kind & ~(MASK_CAUSAL | MASK_KEY_PADDING):
+        raise ValueError(f"unknown mask bits in {mask_kind}")
+    if (mask_kind & MASK_KEY_PADDING) and kv_lens is None:
+        raise ValueError("key padding needs kv_lens")
+    scale = _as_scale(scale)
+    O = np.zeros((B, H, Nq, d))
+    L = np.full((B, H, Nq), -np.inf)
+    for b in range(B):
+        n_vis = _kv_len(mask_kind, kv_lens, b, Nk)
+        vis = visible_general(Nq, Nk, bool(mask_kind & MASK_CAUSAL), window_left, n_vis)
+        ok = vis.any(axis=1)
+        for h in range(H):
+            s = np.where(vis, (q[b, h] @ k[b, h].T) * scale, -np.inf)
+            m = s[ok].max(axis=1)
+            e = np.exp(s[ok] - m[:, None])
+            l = e.sum(axis=1)
+            O[b, h, ok] = (e @ v[b, h]) / l[:, None]
+            L[b, h, ok] = m + np.log(l)
+    return O, L
