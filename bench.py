@@ -91,6 +91,31 @@ def cpu_baseline(x, wl, o_gpu):
                       f"{cores} worker threads with single-threaded BLAS"}, parity
 
 
+def cpu_baseline_window(x, wl, o_gpu_rows, rows):
+    """Time the general oracle on a row sample of a sliding-window workload
+    (every head, the query rows ``rows``) and check the GPU rows against it;
+    the rate credits 4*d flops per visible (query, key) pair of the sample."""
+    from fa_inputs import inputs_f64
+    from oracle import attention_general_ref
+    q, k, v = inputs_f64(x)
+    t0 = time.perf_counter()
+    Or, Lr = attention_general_ref(q, k, v, wl.scale, wl.mask_kind, wl.window_left,
+                                   x["kv_lens"], rows=rows)
+    dt = time.perf_counter() - t0
+    a = rows                    # N_q = N_k: query r sits at key position r
+    lo = np.maximum(0, a - wl.window_left) if wl.window_left >= 0 else np.zeros_like(a)
+    hi = a + 1 if (wl.mask_kind & 1) else np.full_like(a, wl.N)
+    flops = 4.0 * wl.d * wl.B * wl.H * float(np.sum(hi - lo))
+    err = np.abs(o_gpu_rows - Or)
+    parity = {"o_max_abs": float(err.max()),
+              "o_rel_frobenius": float(np.linalg.norm(o_gpu_rows - Or) / np.linalg.norm(Or)),
+              "rows_checked": int(len(rows) * wl.B * wl.H)}
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"{len(rows)} evenly spaced query rows of each of the {wl.B * wl.H} "
+                      "heads (full key rows, masked), fp64 NumPy/BLAS"}, parity
+
+
 def cpu_baseline_bwd(x, wl, g):
     """Time the backward oracle on the host (all heads) and check the GPU
     gradients against it on the same bytes."""
@@ -227,10 +252,11 @@ def main():
         return
 
     import exact_attention_92_amd as fa
-    from fa_inputs import (BENCH_WORKLOAD, FP8_WORKLOADS, WORKLOADS, bf16_bits_to_f32,
-                           make_bwd_inputs, make_inputs)
+    from fa_inputs import (BENCH_WORKLOAD, FP8_WORKLOADS, GENERAL_WORKLOADS, WORKLOADS,
+                           bf16_bits_to_f32, make_bwd_inputs, make_inputs)
 
-    wl = {**WORKLOADS, **FP8_WORKLOADS}[args.workload or BENCH_WORKLOAD]
+    wl = {**WORKLOADS, **FP8_WORKLOADS, **GENERAL_WORKLOADS}[args.workload or BENCH_WORKLOAD]
+    general = wl.name in GENERAL_WORKLOADS
     bwd = args.which == "bwd"
     if bwd and wl.dtype != "bf16":
         print("--pass bwd runs the bf16 backward; pick a bf16 workload", file=sys.stderr)
@@ -250,7 +276,16 @@ def main():
                     device=dev)
     lse = torch.empty((wl.B, wl.H, wl.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    if wl.dtype == "fp8":
+    if general:
+        if wl.layout == "bnhd":     # same values, stored [B, N, H, d]; [B, H, N, d] views
+            q, k, v = (t.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3) for t in (q, k, v))
+            o = torch.empty((wl.B, wl.N, wl.H, wl.d), dtype=torch.bfloat16,
+                            device=dev).permute(0, 2, 1, 3)
+
+        def step():
+            fa.fa_fwd_general(q, k, v, o, lse, wl.scale, wl.mask_kind, wl.window_left, kv,
+                              stream.cuda_stream)
+    elif wl.dtype == "fp8":
         qs, ks, vs = (up(x[n + "_descale"]) for n in "qkv")
 
         def step():
@@ -322,12 +357,14 @@ def main():
         "pct_of_peak": round(100.0 * value / peak, 2),
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d,
                    "mask": {0: "none", 1: "causal", 2: "key_padding"}[wl.mask_kind],
+                   **({"window_left": wl.window_left, "layout": wl.layout} if general else {}),
                    "scale": wl.scale, "q_mult": wl.q_mult, "seed": wl.seed,
                    "flops_per_step": flops, "device": torch.cuda.get_device_name(dev)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel": {"bf16": "fa_fwd_bf16_kernel", "f32": "fa_fwd_f32_kernel",
-                                "fp8": "fa_fwd_fp8_kernel"}[wl.dtype],
+                                "fp8": "fa_fwd_fp8_kernel"}[wl.dtype]
+                     + (" (general layout)" if general else ""),
                      "avg_launch_us": round(avg_launch_ms * 1e3, 2),
                      "min_launch_us": round(min(launch_ms) * 1e3, 2)},
         "cpu_baseline": None,
@@ -344,9 +381,14 @@ def main():
             bits = t.view(torch.int16).cpu().numpy().view(np.uint16)
             g[name] = bf16_bits_to_f32(bits).astype(np.float64)
         rec["cpu_baseline"], rec["parity_vs_oracle"] = cpu_baseline_bwd(x, wl, g)
+    elif not args.no_cpu_baseline and wl.window_left >= 0:
+        rows = np.unique(np.linspace(0, wl.N - 1, 1536).astype(np.int64))
+        bits = o[:, :, torch.from_numpy(rows).to(dev)].contiguous().view(torch.int16)
+        o_rows = bf16_bits_to_f32(bits.cpu().numpy().view(np.uint16)).astype(np.float64)
+        rec["cpu_baseline"], rec["parity_vs_oracle"] = cpu_baseline_window(x, wl, o_rows, rows)
     elif not args.no_cpu_baseline:
         if o.dtype == torch.bfloat16:
-            bits = o.view(torch.int16).cpu().numpy().view(np.uint16)
+            bits = o.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
             o_host = bf16_bits_to_f32(bits).astype(np.float64)
         else:
             o_host = o.cpu().numpy().astype(np.float64)

@@ -11,6 +11,9 @@ Names follow the C ABI of ``include/fa_api.h``:
 * ``fa_fwd(q, k, v, o, lse, scale, mask_kind=0, kv_lens=None, stream=None)``
   -- bf16 tensors ``[B, H, N, d]``
 * ``fa_fwd_f32(...)`` -- the same with float32 tensors
+* ``fa_fwd_general(q, k, v, o, lse, scale, mask_kind=0, window_left=-1,
+  kv_lens=None, stream=None)`` -- bf16 with Nq != Nk, a sliding window and
+  any tensor strides (q, o [B, H, Nq, d] and k, v [B, H, Nk, d] views)
 * ``fa_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, o, lse, scale,
   mask_kind=0, kv_lens=None, stream=None)`` -- E4M3 codes (uint8 tensors)
   with per-(batch, head) float32 scales; o is bf16
@@ -39,7 +42,7 @@ FA_ERR_UNSUPPORTED = -2
 FA_ERR_HIP = -3
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa92.so")
-EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_bwd", "fa_decode_paged",
+EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_general", "fa_fwd_fp8", "fa_bwd", "fa_decode_paged",
            "fa_decode_paged_workspace_bytes", "fa_strerror")
 
 _lib = None
@@ -66,6 +69,8 @@ def load_library():
         fn = getattr(lib, name)
         fn.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, vp]
         fn.restype = i32
+    lib.fa_fwd_general.argtypes = [vp] * 5 + [i32] * 5 + [vp] * 4 + [f32, i32, i32, vp, vp]
+    lib.fa_fwd_general.restype = i32
     lib.fa_fwd_fp8.argtypes = [vp] * 8 + [i32, i32, i32, i32, f32, i32, vp, vp]
     lib.fa_fwd_fp8.restype = i32
     lib.fa_decode_paged.argtypes = [vp] * 8 + [i32] * 6 + [f32, vp]
@@ -133,6 +138,34 @@ def _stream_handle(stream, device):
     if stream is None:
         return torch.cuda.current_stream(device).cuda_stream
     return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def fa_fwd_general(q, k, v, o, lse, scale, mask_kind=FA_MASK_NONE, window_left=-1,
+                   kv_lens=None, stream=None):
+    """bf16 forward with Nq != Nk, a sliding window and strided views: q, o
+    [B, H, Nq, d] and k, v [B, H, Nk, d] tensors (any strides whose last
+    dimension is contiguous); lse contiguous float32 [B, H, Nq]."""
+    import torch
+    lib = load_library()
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    strides = []
+    for nm, t, rows in (("q", q, Nq), ("k", k, Nk), ("v", v, Nk), ("o", o, Nq)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise TypeError(f"{nm} must be a bf16 device tensor")
+        if tuple(t.shape) != (B, H, rows, d) or t.stride(3) != 1:
+            raise ValueError(f"{nm} must be [B, H, {rows}, d] with a contiguous last dimension")
+        strides.append((ctypes.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2)))
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, H, Nq):
+        raise ValueError("lse must be a contiguous float32 device tensor [B, H, Nq]")
+    if kv_lens is not None and (kv_lens.dtype != torch.int32 or kv_lens.numel() != B):
+        raise ValueError("kv_lens must be an int32 device tensor [B]")
+    st = lib.fa_fwd_general(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d,
+                            *[ctypes.cast(a, ctypes.c_void_p) for a in strides], float(scale),
+                            int(mask_kind), int(window_left), _ptr(kv_lens),
+                            ctypes.c_void_p(_stream_handle(stream, q.device)))
+    if st != FA_OK:
+        raise FaError(st, fa_strerror(st))
 
 
 def fa_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, o, lse, scale, mask_kind=FA_MASK_NONE,

@@ -180,10 +180,16 @@ struct Params {
   void* o;
   float* lse;
   const int32_t* kv_lens;
-  int H, N, nqb;
+  int H, N, nqb;    // N: query rows (and keys, unless the general layout is used)
   float c;          // |scale| * log2(e), >= kMinScale * log2(e)
   unsigned qsign;   // sign flip applied to Q when scale < 0
   int causal;
+  // General layout only: key count, key position of query row 0 (Nk - Nq),
+  // sliding window (-1: none), batch/head strides (elements) and row
+  // strides (bytes for q, k, v; elements for o).
+  int Nk, off, window;
+  long long qbs, qhs, kbs, khs, vbs, vhs, obs, ohs;
+  unsigned qrs, krs, vrs, ors;
 };
 
 // ---------------------------------------------------------------------------
@@ -197,7 +203,11 @@ struct Params {
 #endif
 
 
-template <int D, int NW>
+// GEN: the general layout (N_q != N_k with the queries at the last N_q key
+// positions, sliding window, arbitrary batch/head/row strides).  Without it
+// every one of those is a compile-time constant of the contiguous
+// self-attention case.
+template <int D, int NW, bool GEN>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(FA_WAVES_PER_EU)))
 void fa_fwd_bf16_kernel(Params p) {
   constexpr int kThreads = 64 * NW;
@@ -229,27 +239,36 @@ void fa_fwd_bf16_kernel(Params p) {
   int bh, qb;
   map_block(p.nqb, causal, bh, qb);
   const int b = bh / p.H;
+  const int Nk = GEN ? p.Nk : N;
+  const int off = GEN ? p.off : 0;          // key position of query row 0
+  const int W = GEN ? p.window : -1;        // keys visible before a query's own position
+  const uint32_t QRB = GEN ? p.qrs : ROWB;  // row strides in bytes
+  const uint32_t KRB = GEN ? p.krs : ROWB;
+  const uint32_t VRB = GEN ? p.vrs : ROWB;
   const size_t hoff = (size_t)bh * (size_t)N * D;
-  const uint16_t* Qh = (const uint16_t*)p.q + hoff;
-  const uint16_t* Kh = (const uint16_t*)p.k + hoff;
-  const uint16_t* Vh = (const uint16_t*)p.v + hoff;
+  const int hh = bh - b * p.H;
+  const uint16_t* Qh = (const uint16_t*)p.q + (GEN ? b * p.qbs + hh * p.qhs : (long long)hoff);
+  const uint16_t* Kh = (const uint16_t*)p.k + (GEN ? b * p.kbs + hh * p.khs : (long long)hoff);
+  const uint16_t* Vh = (const uint16_t*)p.v + (GEN ? b * p.vbs + hh * p.vhs : (long long)hoff);
 
-  int n_vis = N;
+  int n_vis = Nk;
   if (p.kv_lens) {
     const int kl = p.kv_lens[b];
-    n_vis = kl < 0 ? 0 : (kl > N ? N : kl);
+    n_vis = kl < 0 ? 0 : (kl > Nk ? Nk : kl);
   }
   const int q0 = qb * BM;
   const int qw0 = q0 + wave * 32;
-  const int kend = causal ? min(n_vis, q0 + BM) : n_vis;
+  const int kend = causal ? min(n_vis, q0 + BM + off) : n_vis;
   const int nblk = (kend + BN - 1) / BN;
+  // With a window, blocks entirely before the first row's window are skipped.
+  const int jstart = (W >= 0) ? max(0, q0 + off - W) / BN : 0;
 
   // Q rows of this wave in the B-operand layout of S^T = K Q^T.  Rows past N
   // lie outside the buffer range and read as zero.
   u32x4_t qr[KS];
   {
-    const rsrc_t rq = make_rsrc(Qh, (uint32_t)N * ROWB);
-    const uint32_t qoff = (uint32_t)(qw0 + n) * ROWB + 16u * hf;
+    const rsrc_t rq = make_rsrc(Qh, (uint32_t)N * QRB);
+    const uint32_t qoff = (uint32_t)(qw0 + n) * QRB + 16u * hf;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qr[ks] = buf_load16(rq, qoff + 32u * ks) ^ p.qsign;
   }
@@ -262,21 +281,21 @@ void fa_fwd_bf16_kernel(Params p) {
 #pragma unroll
   for (int u = 0; u < KU; ++u) {
     const int unit = tid + u * kThreads;
-    k_off[u] = (uint32_t)(unit / CPR) * ROWB + 16u * (unit % CPR);
+    k_off[u] = (uint32_t)(unit / CPR) * KRB + 16u * (unit % CPR);
   }
   const bool v_unit = tid < VUNITS;   // VUNITS <= kThreads: one piece per thread at most
   const int vkg = tid % (BN / 4), vdc = tid / (BN / 4);
-  const uint32_t v_off = (uint32_t)(4 * vkg) * ROWB + 16u * vdc;
+  const uint32_t v_off = (uint32_t)(4 * vkg) * VRB + 16u * vdc;
   u32x4_t kreg[KU], vreg[4];
   auto load_block = [&](int j) {
     const int kbase = j * BN;
-    const rsrc_t rk = make_rsrc(Kh + (size_t)kbase * D, (uint32_t)max(0, N - kbase) * ROWB);
-    const rsrc_t rv = make_rsrc(Vh + (size_t)kbase * D, (uint32_t)max(0, n_vis - kbase) * ROWB);
+    const rsrc_t rk = make_rsrc(Kh + (size_t)kbase * (KRB / 2), (uint32_t)max(0, Nk - kbase) * KRB);
+    const rsrc_t rv = make_rsrc(Vh + (size_t)kbase * (VRB / 2), (uint32_t)max(0, n_vis - kbase) * VRB);
 #pragma unroll
     for (int u = 0; u < KU; ++u) kreg[u] = buf_load16(rk, k_off[u]);
     if (v_unit) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vreg[i] = buf_load16(rv, v_off + i * ROWB);
+      for (int i = 0; i < 4; ++i) vreg[i] = buf_load16(rv, v_off + i * VRB);
     }
   };
   auto store_block = [&](int buf) {
@@ -337,18 +356,19 @@ void fa_fwd_bf16_kernel(Params p) {
     rs = rs0 + rs1;
   };
 
-  if (nblk > 0) {
-    load_block(0);
+  if (jstart < nblk) {
+    load_block(jstart);
     store_block(0);
   }
   __syncthreads();
 
-  for (int j = 0; j < nblk; ++j) {
-    const int buf = j & 1;
+  for (int j = jstart; j < nblk; ++j) {
+    const int buf = (j - jstart) & 1;
     const bool more = j + 1 < nblk;
     if (more) load_block(j + 1);
     const int kbase = j * BN;
-    const bool wave_skip = causal && (kbase > qw0 + 31);
+    const bool wave_skip = (causal && (kbase > qw0 + 31 + off)) ||
+                           (W >= 0 && kbase + BN - 1 < qw0 + off - W);
     if (!wave_skip) {
       // S^T = K_j Q^T with K rows permuted (row 32kt + krow feeds MFMA row n).
       f32x16_t s[KT];
@@ -372,14 +392,18 @@ void fa_fwd_bf16_kernel(Params p) {
       for (int i = 0; i < VPRE; ++i)
         vpre[i] = *(const u32x4_t*)&vt_lds[buf][32 * (i % DT) + n][16 * (i / DT) + 8 * hf];
       // Register r of key tile kt holds key kbase + 32kt + 16(r/8) + 8hf + r%8.
-      if ((causal && kbase + BN - 1 > qw0) || kbase + BN > n_vis) {
+      if ((causal && kbase + BN - 1 > qw0 + off) || kbase + BN > n_vis ||
+          (W >= 0 && kbase < qw0 + 31 + off - W)) {
         const int qrow = qw0 + n;
-        const int lim = (causal ? min(qrow, n_vis - 1) : n_vis - 1) - kbase - 8 * hf;
+        const int lim = (causal ? min(qrow + off, n_vis - 1) : n_vis - 1) - kbase - 8 * hf;
+        const int lim_lo = (W >= 0) ? qrow + off - W - kbase - 8 * hf : -BN;
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (32 * kt + 16 * (r >> 3) + (r & 7) > lim) s[kt][r] = -INFINITY;
+          for (int r = 0; r < 16; ++r) {
+            const int idx = 32 * kt + 16 * (r >> 3) + (r & 7);
+            if (idx > lim || idx < lim_lo) s[kt][r] = -INFINITY;
+          }
       }
 
       // Exponentials against the reference max.  A wave's first block, or a
@@ -431,14 +455,15 @@ void fa_fwd_bf16_kernel(Params p) {
   }
 
   // Epilogue: O = acc / l (rounded to bf16 once), LSE = (m + log2 le) * ln 2.
-  uint16_t* __restrict__ Oh = (uint16_t*)p.o + hoff;
+  uint16_t* __restrict__ Oh =
+      (uint16_t*)p.o + (GEN ? b * p.obs + hh * p.ohs : (long long)hoff);
   float* __restrict__ Lh = p.lse + (size_t)bh * N;
   const float lt = pair_sum(l_run);
   const float le = pair_sum(le_run);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const int qrow = qw0 + n;
   if (qrow < N) {
-    uint16_t* orow = Oh + (size_t)qrow * D;
+    uint16_t* orow = Oh + (size_t)qrow * (GEN ? (size_t)p.ors : (size_t)D);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -618,7 +643,7 @@ int check_args(const void* q, const void* k, const void* v, const void* o, const
 
 Params make_params(const void* q, const void* k, const void* v, void* o, float* lse, int H, int N,
                    int nqb, float scale, int mask_kind, const int32_t* kv_lens) {
-  Params p;
+  Params p = {};
   p.q = q;
   p.k = k;
   p.v = v;
@@ -657,11 +682,69 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
   const Params p = make_params(q, k, v, o, lse, H, N, nqb, scale, mask_kind, kv_lens);
   const dim3 grid((unsigned)(B * H * nqb)), block(big ? 512 : 256);
   if (d == 128) {
-    if (big) hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, 8>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, 4>), grid, block, 0, s, p);
+    if (big) hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, 8, false>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, 4, false>), grid, block, 0, s, p);
   } else {
-    if (big) hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, 8>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, 4>), grid, block, 0, s, p);
+    if (big) hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, 8, false>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, 4, false>), grid, block, 0, s, p);
+  }
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" int fa_fwd_general(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int B, int H, int Nq, int Nk, int d, const int64_t* q_strides,
+                              const int64_t* k_strides, const int64_t* v_strides,
+                              const int64_t* o_strides, float scale, int mask_kind,
+                              int window_left, const int32_t* kv_lens, void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  const uintptr_t al = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse;
+  if (al & 15u) return FA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || window_left < -1) return FA_ERR_INVALID_ARG;
+  if (mask_kind & ~(FA_MASK_CAUSAL | FA_MASK_KEY_PADDING)) return FA_ERR_INVALID_ARG;
+  if ((mask_kind & FA_MASK_KEY_PADDING) && !kv_lens) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  // Strides (elements): NULL = contiguous [B, H, rows, d].  Rows must be
+  // 16-byte aligned and hold d contiguous elements; batch and head starts
+  // 16-byte aligned.
+  int64_t st[4][3];
+  const int64_t* given[4] = {q_strides, k_strides, v_strides, o_strides};
+  const int rows[4] = {Nq, Nk, Nk, Nq};
+  for (int t = 0; t < 4; ++t) {
+    if (given[t]) {
+      for (int i = 0; i < 3; ++i) st[t][i] = given[t][i];
+    } else {
+      st[t][2] = d;
+      st[t][1] = (int64_t)rows[t] * d;
+      st[t][0] = (int64_t)H * rows[t] * d;
+    }
+    if (st[t][2] < d || st[t][0] < 0 || st[t][1] < 0) return FA_ERR_INVALID_ARG;
+    if ((st[t][0] | st[t][1] | st[t][2]) & 7) return FA_ERR_INVALID_ARG;
+    // A head's rows (plus a block past the end) use 32-bit byte offsets.
+    if (((long long)rows[t] + 256) * st[t][2] * 2 > 0xffffffffLL) return FA_ERR_INVALID_ARG;
+  }
+  const bool causal = (mask_kind & FA_MASK_CAUSAL) != 0;
+  const long long grid256 = (long long)B * H * ((Nq + 255) / 256);
+  const bool big = grid256 >= (causal ? 2 : 1) * kCUs;
+  const int BM = big ? 256 : 128;
+  const int nqb = (Nq + BM - 1) / BM;
+  if ((long long)B * H * nqb > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  Params p = make_params(q, k, v, o, lse, H, Nq, nqb, scale, mask_kind, kv_lens);
+  p.Nk = Nk;
+  p.off = Nk - Nq;
+  p.window = window_left;
+  p.qbs = st[0][0]; p.qhs = st[0][1]; p.qrs = (unsigned)(st[0][2] * 2);
+  p.kbs = st[1][0]; p.khs = st[1][1]; p.krs = (unsigned)(st[1][2] * 2);
+  p.vbs = st[2][0]; p.vhs = st[2][1]; p.vrs = (unsigned)(st[2][2] * 2);
+  p.obs = st[3][0]; p.ohs = st[3][1]; p.ors = (unsigned)st[3][2];
+  const dim3 grid((unsigned)(B * H * nqb)), block(big ? 512 : 256);
+  hipStream_t s = (hipStream_t)stream;
+  if (d == 128) {
+    if (big) hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, 8, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, 4, true>), grid, block, 0, s, p);
+  } else {
+    if (big) hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, 8, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, 4, true>), grid, block, 0, s, p);
   }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

@@ -62,6 +62,8 @@ class Workload:
     q_mult: float = 1.0
     kv_len_range: Optional[Tuple[int, int]] = None
     note: str = field(default="", compare=False)
+    window_left: int = -1      # sliding window (general forward only)
+    layout: str = "bhnd"       # "bnhd": tensors stored [B, N, H, d] (general forward only)
 
     @property
     def scale(self) -> float:
@@ -69,7 +71,15 @@ class Workload:
         return float(np.float32(1.0 / np.sqrt(self.d)))
 
     def flops(self) -> float:
-        """Forward FLOPs by the metric's formula: 4*B*H*N^2*d, halved when causal."""
+        """Forward FLOPs by the metric's formula: 4*B*H*N^2*d, halved when causal.
+        With a sliding window: 4*d per visible (query, key) pair."""
+        if self.window_left >= 0:
+            W, N = self.window_left, self.N
+            if self.mask_kind & MASK_CAUSAL:
+                pairs = (W + 1) * N - W * (W + 1) / 2.0 if W < N else N * (N + 1) / 2.0
+            else:
+                pairs = sum(N - max(0, r - W) for r in range(N))
+            return 4.0 * self.B * self.H * pairs * self.d
         f = 4.0 * self.B * self.H * self.N * self.N * self.d
         return f / 2.0 if (self.mask_kind & MASK_CAUSAL) else f
 
@@ -132,6 +142,16 @@ DECODE_WORKLOADS = {
         "decode_b32h32_d128_bs64_len1k8k", 32, 32, 128, 64, (1024, 8192), seed=6),
 }
 
+
+# Workloads of the general forward (strided layouts, sliding windows).
+GENERAL_WORKLOADS = {
+    "bf16_b1h8_n65536_d128_causal_w4096": Workload(
+        "bf16_b1h8_n65536_d128_causal_w4096", 1, 8, 65536, 128, "bf16", MASK_CAUSAL, seed=5,
+        window_left=4096, note="long context, causal, sliding window of 4096 keys"),
+    "bf16_b2h32_n4096_d128_causal_bnhd": Workload(
+        "bf16_b2h32_n4096_d128_causal_bnhd", 2, 32, 4096, 128, "bf16", MASK_CAUSAL, seed=3,
+        q_mult=2.0, layout="bnhd", note="the bench workload stored [B, N, H, d]"),
+}
 
 # The workload the throughput figure is quoted on.
 BENCH_WORKLOAD = "bf16_b2h32_n4096_d128_causal"

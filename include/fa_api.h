@@ -92,6 +92,30 @@ int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int H, int N, int d, float scale, int mask_kind,
                const int32_t* kv_lens, void* stream);
 
+/* General bf16 forward: fa_fwd with separate query and key counts, a
+ * sliding window and arbitrary strides (the variants of the forward that
+ * "FlashAttention 完整解析" §11 and the youngju.dev walkthrough §11 list
+ * for the library: cross-attention lengths, local windows, layouts).
+ *  - q, o: [B, H, Nq, d]; k, v: [B, H, Nk, d], each addressed through its
+ *    own strides: HOST int64 arrays {batch, head, row} in elements (NULL:
+ *    contiguous).  Rows hold d contiguous elements; every stride is a
+ *    multiple of 8 elements (16 bytes) and the row stride at least d, so
+ *    e.g. the [B, N, H, d] layout is strides {N*H*d, d, H*d}.  lse is a
+ *    contiguous float32 [B, H, Nq].
+ *  - Query row r sits at key position a_r = r + Nk - Nq (the queries are the
+ *    last Nq positions of the key sequence).  Key c is visible to row r iff
+ *    c < kv_len (key padding), c <= a_r (FA_MASK_CAUSAL), and
+ *    c >= a_r - window_left when window_left >= 0 (window_left = -1: no
+ *    window).  A row that sees no key gets O = 0, LSE = -inf.
+ *  - Nq, Nk >= 1; d is 64 or 128; 16-byte aligned pointers; other
+ *    conventions (scale, kv_lens, stream, errors) as for fa_fwd.  With
+ *    contiguous strides, Nq = Nk and no window it computes exactly fa_fwd. */
+int fa_fwd_general(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int Nq, int Nk, int d, const int64_t* q_strides,
+                   const int64_t* k_strides, const int64_t* v_strides,
+                   const int64_t* o_strides, float scale, int mask_kind, int window_left,
+                   const int32_t* kv_lens, void* stream);
+
 /* FP8 forward (the FP8 path of "FlashAttention 完整解析" §5.5 and of the
  * youngju.dev walkthrough §9.2): q, k, v hold OCP FP8 E4M3 codes
  * ("e4m3fn": bias 7, largest finite 448, no infinities) of shape

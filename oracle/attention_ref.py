@@ -300,8 +300,10 @@ def brute_ref(q, k, v, scale, mask_kind=MASK_NONE, kv_lens=None):
 # General masks: N_q != N_k, sliding window.
 # ---------------------------------------------------------------------------
 
-def visible_general(Nq: int, Nk: int, causal: bool, window_left: int, n_vis: int):
-    """Boolean [Nq, Nk] visibility for the general forward.
+def visible_general(Nq: int, Nk: int, causal: bool, window_left: int, n_vis: int,
+                    rows=None):
+    """Boolean [Nq, Nk] visibility for the general forward (only the query
+    rows ``rows`` when given: [len(rows), Nk]).
 
     Query r sits at key position a_r = r + (Nk - Nq) (the queries are the last
     Nq positions of the key sequence).  Key c is visible to query r iff
@@ -309,22 +311,26 @@ def visible_general(Nq: int, Nk: int, causal: bool, window_left: int, n_vis: int
     window_left >= 0 (a window of window_left keys before the query's own
     position).
     """
-    r = np.arange(Nq)[:, None] + (Nk - Nq)
+    rr = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64)
+    r = rr[:, None] + (Nk - Nq)
     c = np.arange(Nk)[None, :]
     vis = c < n_vis
     if causal:
         vis = vis & (c <= r)
     if window_left >= 0:
         vis = vis & (c >= r - window_left)
-    return np.broadcast_to(vis, (Nq, Nk))
+    return np.broadcast_to(vis, (len(rr), Nk))
 
 
 def attention_general_ref(q, k, v, scale, mask_kind=MASK_NONE, window_left: int = -1,
-                          kv_lens=None):
+                          kv_lens=None, magnitudes: bool = False, rows=None):
     """fp64 O [B, H, Nq, d] and LSE [B, H, Nq] with N_q != N_k allowed and an
     optional sliding window (see visible_general); the same definition as
     attention_ref otherwise (max-subtracted softmax over the visible keys;
-    a row with no visible key has O = 0, LSE = -inf)."""
+    a row with no visible key has O = 0, LSE = -inf).  ``magnitudes=True``
+    appends P |V| [B, H, Nq, d] (for tolerances).  ``rows``: optional query
+    row indices; then only those rows are computed and the outputs are
+    [B, H, R, ...] in that order."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -337,17 +343,23 @@ def attention_general_ref(q, k, v, scale, mask_kind=MASK_NONE, window_left: int 
     if (mask_kind & MASK_KEY_PADDING) and kv_lens is None:
         raise ValueError("key padding needs kv_lens")
     scale = _as_scale(scale)
-    O = np.zeros((B, H, Nq, d))
-    L = np.full((B, H, Nq), -np.inf)
+    rows = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64)
+    R = len(rows)
+    O = np.zeros((B, H, R, d))
+    L = np.full((B, H, R), -np.inf)
+    M = np.zeros((B, H, R, d))
     for b in range(B):
         n_vis = _kv_len(mask_kind, kv_lens, b, Nk)
-        vis = visible_general(Nq, Nk, bool(mask_kind & MASK_CAUSAL), window_left, n_vis)
+        vis = visible_general(Nq, Nk, bool(mask_kind & MASK_CAUSAL), window_left, n_vis, rows)
         ok = vis.any(axis=1)
         for h in range(H):
-            s = np.where(vis, (q[b, h] @ k[b, h].T) * scale, -np.inf)
+            s = np.where(vis, (q[b, h, rows] @ k[b, h].T) * scale, -np.inf)
             m = s[ok].max(axis=1)
             e = np.exp(s[ok] - m[:, None])
             l = e.sum(axis=1)
             O[b, h, ok] = (e @ v[b, h]) / l[:, None]
             L[b, h, ok] = m + np.log(l)
+            M[b, h, ok] = (e @ np.abs(v[b, h])) / l[:, None]
+    if magnitudes:
+        return O, L, M
     return O, L

@@ -26,8 +26,9 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared() == ["fa_bwd", "fa_decode_paged", "fa_decode_paged_workspace_bytes", "fa_fwd",
-                           "fa_fwd_f32", "fa_fwd_fp8", "fa_strerror"]
+    assert _declared() == ["fa_bwd", "fa_decode_paged", "fa_decode_paged_workspace_bytes",
+                           "fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_fwd_general",
+                           "fa_strerror"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -144,6 +145,33 @@ def test_decode_invalid_arguments_are_rejected_before_launch(lib):
     assert call(d=96) == fa.FA_ERR_UNSUPPORTED
     assert lib.fa_decode_paged_workspace_bytes(2, 2, 128, 64, 4) == 2 * 2 * 1 * 130 * 4
     assert lib.fa_decode_paged_workspace_bytes(2, 2, 96, 64, 4) == 0
+
+
+def test_general_invalid_arguments_are_rejected_before_launch(lib):
+    import exact_attention_92_amd as fa
+    bad = fa.FA_ERR_INVALID_ARG
+    good = [0x1000 * (i + 1) for i in range(5)]
+
+    def st(*v):
+        return ctypes.cast((ctypes.c_int64 * 3)(*v), ctypes.c_void_p)
+
+    def call(ptrs=good, B=1, H=2, Nq=16, Nk=32, d=64, strides=(None,) * 4, scale=0.1, mask=0,
+             window=-1, kv=None):
+        return lib.fa_fwd_general(*[ctypes.c_void_p(p) if p is not None else None for p in ptrs],
+                                  B, H, Nq, Nk, d, *strides, ctypes.c_float(scale), mask, window,
+                                  ctypes.c_void_p(kv) if kv else None, None)
+    for i in range(5):
+        p = list(good)
+        p[i] = None
+        assert call(p) == bad
+        p[i] = good[i] + 8
+        assert call(p) == bad
+    assert call(Nq=0) == bad and call(Nk=0) == bad and call(window=-2) == bad
+    assert call(mask=fa.FA_MASK_KEY_PADDING) == bad and call(scale=float("nan")) == bad
+    assert call(strides=(st(0, 0, 32), None, None, None)) == bad        # row stride < d
+    assert call(strides=(st(0, 3, 64), None, None, None)) == bad        # misaligned head stride
+    assert call(strides=(None, st(0, 0, 1 << 40), None, None)) == bad   # rows beyond 32-bit offsets
+    assert call(d=96) == fa.FA_ERR_UNSUPPORTED
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -113,8 +113,8 @@ def test_visibility_alignment():
 
 
 MUTATIONS = {
-    "alignment top-left instead of bottom-right": ("r = np.arange(Nq)[:, None] + (Nk - Nq)",
-                                                   "r = np.arange(Nq)[:, None]"),
+    "alignment top-left instead of bottom-right": ("r = rr[:, None] + (Nk - Nq)",
+                                                   "r = rr[:, None]"),
     "window one key short": ("vis = vis & (c >= r - window_left)",
                              "vis = vis & (c > r - window_left)"),
     "window on the wrong side": ("vis = vis & (c >= r - window_left)",
@@ -145,3 +145,17 @@ def test_planted_mistakes_are_caught(name):
     # The reference values come from the brute force (test_brute_force_tiny); here we only
     # check the mutated oracle differs from the pinned one on those inputs.
     assert caught, name
+
+
+def test_row_subset_matches_full_rows():
+    """Computing only some query rows gives exactly those rows of the full
+    result (the row sample used at long sequence lengths)."""
+    q, k, v = _rand(2, 2, 9, 13, 4, seed=8)
+    kv = np.array([11, 6], dtype=np.int32)
+    rows = np.array([8, 0, 3, 5])
+    for mask in MASKS:
+        for window in (-1, 0, 3):
+            O, L = attention_general_ref(q, k, v, 0.7, mask, window, kv)
+            Os, Ls = attention_general_ref(q, k, v, 0.7, mask, window, kv, rows=rows)
+            np.testing.assert_array_equal(Os, O[:, :, rows])
+            np.testing.assert_array_equal(Ls, L[:, :, rows])
