@@ -363,3 +363,46 @@ def attention_general_ref(q, k, v, scale, mask_kind=MASK_NONE, window_left: int 
     if magnitudes:
         return O, L, M
     return O, L
+
+
+def attention_varlen_ref(q, k, v, cu_q, cu_k, scale, mask_kind=MASK_NONE,
+                         window_left: int = -1, magnitudes: bool = False):
+    """fp64 attention over packed variable-length sequences.
+
+    q: [total_q, H, d]; k, v: [total_k, H, d]; cu_q, cu_k: int [B + 1]
+    sequence boundaries.  Sequence b is the query rows cu_q[b]:cu_q[b+1]
+    attending to the key rows cu_k[b]:cu_k[b+1] on its own, with the
+    conventions of attention_general_ref (queries at the last positions of
+    the sequence's keys; causal and window act within the sequence).
+    Returns O [total_q, H, d] and LSE [H, total_q] (and P |V| [total_q, H, d]
+    with ``magnitudes``).  Rows not covered by any sequence stay NaN.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    total_q, H, d = q.shape
+    O = np.full((total_q, H, d), np.nan)
+    L = np.full((H, total_q), np.nan)
+    M = np.full((total_q, H, d), np.nan)
+    if mask_kind & ~MASK_CAUSAL:
+        raise ValueError("packed sequences take their key lengths from cu_k: causal bit only")
+    for b in range(len(cu_q) - 1):
+        qs, qe, ks, ke = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        if qe <= qs:
+            continue
+        if ke <= ks:                       # no keys: every row is empty
+            O[qs:qe] = 0.0
+            L[:, qs:qe] = -np.inf
+            M[qs:qe] = 0.0
+            continue
+        qb = q[qs:qe].transpose(1, 0, 2)[None]     # [1, H, n_q, d]
+        kb = k[ks:ke].transpose(1, 0, 2)[None]
+        vb = v[ks:ke].transpose(1, 0, 2)[None]
+        Ob, Lb, Mb = attention_general_ref(qb, kb, vb, scale, mask_kind, window_left,
+                                           magnitudes=True)
+        O[qs:qe] = Ob[0].transpose(1, 0, 2)
+        L[:, qs:qe] = Lb[0]
+        M[qs:qe] = Mb[0].transpose(1, 0, 2)
+    if magnitudes:
+        return O, L, M
+    return O, L
