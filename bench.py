@@ -116,6 +116,30 @@ def cpu_baseline_window(x, wl, o_gpu_rows, rows):
                       "heads (full key rows, masked), fp64 NumPy/BLAS"}, parity
 
 
+def cpu_baseline_varlen(x, wl, o_gpu, nseq=4):
+    """Time the packed-sequence oracle on the first ``nseq`` sequences (all
+    heads) and check the GPU rows of those sequences against it."""
+    from fa_inputs import to_f64
+    from oracle import attention_varlen_ref
+    cu_q, cu_k = x["cu_q"][:nseq + 1], x["cu_k"][:nseq + 1]
+    q = to_f64(x["q"][:cu_q[-1]])
+    k, v = to_f64(x["k"][:cu_k[-1]]), to_f64(x["v"][:cu_k[-1]])
+    t0 = time.perf_counter()
+    Or, _ = attention_varlen_ref(q, k, v, cu_q, cu_k, wl.scale, wl.mask_kind, wl.window_left)
+    dt = time.perf_counter() - t0
+    n = np.diff(cu_q).astype(np.float64)
+    pairs = n * (n + 1) / 2.0 if wl.mask_kind & 1 else n * n
+    flops = 4.0 * wl.H * wl.d * float(pairs.sum())
+    og = o_gpu[:cu_q[-1]]
+    parity = {"o_max_abs": float(np.abs(og - Or).max()),
+              "o_rel_frobenius": float(np.linalg.norm(og - Or) / np.linalg.norm(Or)),
+              "rows_checked": int(cu_q[-1]) * wl.H}
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"the first {nseq} of the {wl.B} packed sequences (lengths "
+                      f"{np.diff(cu_q).tolist()}), all {wl.H} heads, fp64 NumPy/BLAS"}, parity
+
+
 def cpu_baseline_bwd(x, wl, g):
     """Time the backward oracle on the host (all heads) and check the GPU
     gradients against it on the same bytes."""
@@ -270,13 +294,21 @@ def main():
         return torch.from_numpy(a).to(dev)
 
     q, k, v = up(x["q"]), up(x["k"]), up(x["v"])
-    kv = None if x["kv_lens"] is None else torch.from_numpy(x["kv_lens"]).to(dev)
-    shape = (wl.B, wl.H, wl.N, wl.d)
+    varlen = wl.layout == "varlen"
+    kv = None if varlen or x["kv_lens"] is None else torch.from_numpy(x["kv_lens"]).to(dev)
+    shape = tuple(q.shape) if varlen else (wl.B, wl.H, wl.N, wl.d)
     o = torch.empty(shape, dtype=torch.float32 if wl.dtype == "f32" else torch.bfloat16,
                     device=dev)
-    lse = torch.empty((wl.B, wl.H, wl.N), dtype=torch.float32, device=dev)
+    lse = torch.empty((wl.H, q.shape[0]) if varlen else (wl.B, wl.H, wl.N),
+                      dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    if general:
+    if varlen:
+        cu_q, cu_k = (torch.from_numpy(x[n]).to(dev) for n in ("cu_q", "cu_k"))
+
+        def step():
+            fa.fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, wl.N, wl.scale, wl.mask_kind,
+                             wl.window_left, stream.cuda_stream)
+    elif general:
         if wl.layout == "bnhd":     # same values, stored [B, N, H, d]; [B, H, N, d] views
             q, k, v = (t.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3) for t in (q, k, v))
             o = torch.empty((wl.B, wl.N, wl.H, wl.d), dtype=torch.bfloat16,
@@ -358,6 +390,7 @@ def main():
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "d": wl.d,
                    "mask": {0: "none", 1: "causal", 2: "key_padding"}[wl.mask_kind],
                    **({"window_left": wl.window_left, "layout": wl.layout} if general else {}),
+                   **({"seq_lens": np.diff(x["cu_q"]).tolist()} if varlen else {}),
                    "scale": wl.scale, "q_mult": wl.q_mult, "seed": wl.seed,
                    "flops_per_step": flops, "device": torch.cuda.get_device_name(dev)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
@@ -381,6 +414,10 @@ def main():
             bits = t.view(torch.int16).cpu().numpy().view(np.uint16)
             g[name] = bf16_bits_to_f32(bits).astype(np.float64)
         rec["cpu_baseline"], rec["parity_vs_oracle"] = cpu_baseline_bwd(x, wl, g)
+    elif not args.no_cpu_baseline and varlen:
+        bits = o.view(torch.int16).cpu().numpy().view(np.uint16)
+        rec["cpu_baseline"], rec["parity_vs_oracle"] = cpu_baseline_varlen(
+            x, wl, bf16_bits_to_f32(bits).astype(np.float64))
     elif not args.no_cpu_baseline and wl.window_left >= 0:
         rows = np.unique(np.linspace(0, wl.N - 1, 1536).astype(np.int64))
         bits = o[:, :, torch.from_numpy(rows).to(dev)].contiguous().view(torch.int16)

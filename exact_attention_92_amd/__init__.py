@@ -42,8 +42,8 @@ FA_ERR_UNSUPPORTED = -2
 FA_ERR_HIP = -3
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa92.so")
-EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_general", "fa_fwd_fp8", "fa_bwd", "fa_decode_paged",
-           "fa_decode_paged_workspace_bytes", "fa_strerror")
+EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_general", "fa_fwd_varlen", "fa_fwd_fp8", "fa_bwd",
+           "fa_decode_paged", "fa_decode_paged_workspace_bytes", "fa_strerror")
 
 _lib = None
 
@@ -71,6 +71,9 @@ def load_library():
         fn.restype = i32
     lib.fa_fwd_general.argtypes = [vp] * 5 + [i32] * 5 + [vp] * 4 + [f32, i32, i32, vp, vp]
     lib.fa_fwd_general.restype = i32
+    lib.fa_fwd_varlen.argtypes = [vp] * 7 + [i32] * 3 + [ctypes.c_int64] * 2 + [i32, f32, i32,
+                                                                               i32, vp]
+    lib.fa_fwd_varlen.restype = i32
     lib.fa_fwd_fp8.argtypes = [vp] * 8 + [i32, i32, i32, i32, f32, i32, vp, vp]
     lib.fa_fwd_fp8.restype = i32
     lib.fa_decode_paged.argtypes = [vp] * 8 + [i32] * 6 + [f32, vp]
@@ -164,6 +167,37 @@ def fa_fwd_general(q, k, v, o, lse, scale, mask_kind=FA_MASK_NONE, window_left=-
                             *[ctypes.cast(a, ctypes.c_void_p) for a in strides], float(scale),
                             int(mask_kind), int(window_left), _ptr(kv_lens),
                             ctypes.c_void_p(_stream_handle(stream, q.device)))
+    if st != FA_OK:
+        raise FaError(st, fa_strerror(st))
+
+
+def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, scale,
+                  mask_kind=FA_MASK_NONE, window_left=-1, stream=None):
+    """bf16 forward over packed sequences: q, o [total_q, H, d] and k, v
+    [total_k, H, d] contiguous; lse float32 [H, total_q]; cu_seqlens_q/k
+    int32 device tensors [B + 1] of sequence boundaries."""
+    import torch
+    lib = load_library()
+    total_q, H, d = q.shape
+    total_k = k.shape[0]
+    for nm, t, rows in (("q", q, total_q), ("k", k, total_k), ("v", v, total_k),
+                        ("o", o, total_q)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise TypeError(f"{nm} must be a contiguous bf16 device tensor")
+        if tuple(t.shape) != (rows, H, d):
+            raise ValueError(f"{nm} must be [{rows}, H, d]")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (H, total_q):
+        raise ValueError("lse must be a contiguous float32 device tensor [H, total_q]")
+    for nm, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous() or t.dim() != 1:
+            raise ValueError(f"{nm} must be a contiguous int32 device tensor [B + 1]")
+    B = cu_seqlens_q.numel() - 1
+    if B < 1 or cu_seqlens_k.numel() != B + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B + 1 >= 2 entries")
+    st = lib.fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens_q),
+                           _ptr(cu_seqlens_k), B, H, d, total_q, total_k, int(max_seqlen_q),
+                           float(scale), int(mask_kind), int(window_left),
+                           ctypes.c_void_p(_stream_handle(stream, q.device)))
     if st != FA_OK:
         raise FaError(st, fa_strerror(st))
 

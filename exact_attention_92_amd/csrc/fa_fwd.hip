@@ -152,10 +152,22 @@ __device__ __forceinline__ void mfma_read_ahead() {
 // masks the last (heaviest) query block of every head first, so the light
 // ones fill the tail.  Otherwise XCD x gets the contiguous logical range
 // [x*G/8, (x+1)*G/8), heavy query blocks first within each head.
-__device__ __forceinline__ void map_block(int nqb, bool causal, int& bh, int& qb) {
+//
+// With spread (packed sequences of unequal lengths, where binding heads to
+// XCDs would bind whole sequences to them), the order is rank-major over all
+// (batch, head): consecutive workgroups, and so the XCDs, take every
+// sequence's blocks of one rank before the next rank.
+__device__ __forceinline__ void map_block(int nqb, bool causal, int& bh, int& qb,
+                                          bool spread = false) {
   const int G = gridDim.x;
   const int w = blockIdx.x;
   const int BH = G / nqb;
+  if (spread) {
+    bh = w % BH;
+    const int r = w / BH;
+    qb = causal ? (nqb - 1 - r) : r;
+    return;
+  }
   if (G % 8 == 0 && BH % 8 == 0) {
     // XCD x = w % 8 owns heads [x*BH/8, (x+1)*BH/8); it visits their query
     // blocks rank by rank (heaviest causal rank first), head by head.
@@ -190,6 +202,12 @@ struct Params {
   int Nk, off, window;
   long long qbs, qhs, kbs, khs, vbs, vhs, obs, ohs;
   unsigned qrs, krs, vrs, ors;
+  // Packed variable-length sequences only: sequence b owns query rows
+  // [cu_q[b], cu_q[b+1]) of total_q and key rows [cu_k[b], cu_k[b+1]) of
+  // total_k; lse is [H, total_q].
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  long long total_q, total_k;
 };
 
 // ---------------------------------------------------------------------------
@@ -203,13 +221,16 @@ struct Params {
 #endif
 
 
-// GEN: the general layout (N_q != N_k with the queries at the last N_q key
-// positions, sliding window, arbitrary batch/head/row strides).  Without it
-// every one of those is a compile-time constant of the contiguous
-// self-attention case.
-template <int D, int NW, bool GEN>
+// MODE 0: contiguous self-attention [B, H, N, d]; every length, offset and
+// stride is a compile-time constant or N.  MODE 1 (general): N_q != N_k with
+// the queries at the last N_q key positions, sliding window, arbitrary
+// batch/head/row strides.  MODE 2 (varlen): MODE 1 over packed sequences
+// whose boundaries are read from cu_q / cu_k.
+template <int D, int NW, int MODE>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(FA_WAVES_PER_EU)))
 void fa_fwd_bf16_kernel(Params p) {
+  constexpr bool GEN = MODE != 0;
+  constexpr bool VL = MODE == 2;
   constexpr int kThreads = 64 * NW;
   constexpr int BN = 64;            // keys per block
   constexpr int BM = 32 * NW;       // query rows per workgroup
@@ -221,9 +242,11 @@ void fa_fwd_bf16_kernel(Params p) {
   constexpr int VLD = BN + 8;       // V^T row stride in LDS (elements)
   constexpr uint32_t ROWB = D * 2;  // bytes per row in device memory
   constexpr int CPR = D / 8;        // 16-byte chunks per row
-  constexpr int KU = BN * CPR / kThreads;    // 16-byte K pieces per thread
+  constexpr int KUNITS = BN * CPR;           // 16-byte K pieces per block
+  constexpr int KU = (KUNITS + kThreads - 1) / kThreads;   // per thread
+  constexpr bool KFULL = KUNITS % kThreads == 0;           // every thread has KU pieces
   constexpr int VUNITS = (BN / 4) * CPR;     // V pieces of 4 keys x 8 dims
-  static_assert(KU >= 1 && (BN * CPR) % kThreads == 0 && VUNITS <= kThreads, "tile shape");
+  static_assert(D % 32 == 0 && VUNITS <= kThreads, "tile shape");
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BN][KLD];
   __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][D][VLD];
@@ -234,22 +257,39 @@ void fa_fwd_bf16_kernel(Params p) {
   const int n = lane & 31;
   const int hf = lane >> 5;
   const bool causal = p.causal != 0;
-  const int N = p.N;
+  int N = p.N;
 
   int bh, qb;
-  map_block(p.nqb, causal, bh, qb);
+  map_block(p.nqb, causal, bh, qb, VL);
   const int b = bh / p.H;
-  const int Nk = GEN ? p.Nk : N;
-  const int off = GEN ? p.off : 0;          // key position of query row 0
+  int Nk = GEN ? p.Nk : N;
+  int off = GEN ? p.off : 0;                // key position of query row 0
+  long long qr0 = 0, kr0 = 0;               // varlen: first packed row of the sequence
+  if (VL) {
+    // Boundaries clamped into the packed tensors, so any cu values stay in bounds.
+    const long long q_s = min(max((long long)p.cu_q[b], 0LL), p.total_q);
+    const long long q_e = min(max((long long)p.cu_q[b + 1], q_s), p.total_q);
+    const long long k_s = min(max((long long)p.cu_k[b], 0LL), p.total_k);
+    const long long k_e = min(max((long long)p.cu_k[b + 1], k_s), p.total_k);
+    N = (int)(q_e - q_s);
+    Nk = (int)(k_e - k_s);
+    off = Nk - N;
+    qr0 = q_s;
+    kr0 = k_s;
+    if (qb * (32 * NW) >= N) return;        // whole workgroup past the sequence's rows
+  }
   const int W = GEN ? p.window : -1;        // keys visible before a query's own position
   const uint32_t QRB = GEN ? p.qrs : ROWB;  // row strides in bytes
   const uint32_t KRB = GEN ? p.krs : ROWB;
   const uint32_t VRB = GEN ? p.vrs : ROWB;
   const size_t hoff = (size_t)bh * (size_t)N * D;
   const int hh = bh - b * p.H;
-  const uint16_t* Qh = (const uint16_t*)p.q + (GEN ? b * p.qbs + hh * p.qhs : (long long)hoff);
-  const uint16_t* Kh = (const uint16_t*)p.k + (GEN ? b * p.kbs + hh * p.khs : (long long)hoff);
-  const uint16_t* Vh = (const uint16_t*)p.v + (GEN ? b * p.vbs + hh * p.vhs : (long long)hoff);
+  const uint16_t* Qh = (const uint16_t*)p.q +
+                       (GEN ? b * p.qbs + hh * p.qhs + qr0 * (QRB / 2) : (long long)hoff);
+  const uint16_t* Kh = (const uint16_t*)p.k +
+                       (GEN ? b * p.kbs + hh * p.khs + kr0 * (KRB / 2) : (long long)hoff);
+  const uint16_t* Vh = (const uint16_t*)p.v +
+                       (GEN ? b * p.vbs + hh * p.vhs + kr0 * (VRB / 2) : (long long)hoff);
 
   int n_vis = Nk;
   if (p.kv_lens) {
@@ -281,7 +321,9 @@ void fa_fwd_bf16_kernel(Params p) {
 #pragma unroll
   for (int u = 0; u < KU; ++u) {
     const int unit = tid + u * kThreads;
-    k_off[u] = (uint32_t)(unit / CPR) * KRB + 16u * (unit % CPR);
+    // A thread without a piece reads past every buffer range (zeros).
+    k_off[u] = (KFULL || unit < KUNITS) ? (uint32_t)(unit / CPR) * KRB + 16u * (unit % CPR)
+                                        : 0x80000000u;
   }
   const bool v_unit = tid < VUNITS;   // VUNITS <= kThreads: one piece per thread at most
   const int vkg = tid % (BN / 4), vdc = tid / (BN / 4);
@@ -302,7 +344,7 @@ void fa_fwd_bf16_kernel(Params p) {
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
       const int unit = tid + u * kThreads;
-      *(u32x4_t*)&k_lds[buf][unit / CPR][8 * (unit % CPR)] = kreg[u];
+      if (KFULL || unit < KUNITS) *(u32x4_t*)&k_lds[buf][unit / CPR][8 * (unit % CPR)] = kreg[u];
     }
     if (v_unit) {
       // Dword w of key i holds dims 8*vdc + 2w, +1: regroup into
@@ -386,7 +428,7 @@ void fa_fwd_bf16_kernel(Params p) {
       mfma_read_ahead<KS * KT, FA_READ_AHEAD>();
       // The first V^T operands are requested now, so they arrive while the
       // softmax runs.
-      constexpr int VPRE = FA_V_PREFETCH;
+      constexpr int VPRE = FA_V_PREFETCH < PC * DT ? FA_V_PREFETCH : PC * DT;
       u32x4_t vpre[VPRE > 0 ? VPRE : 1];
 #pragma unroll
       for (int i = 0; i < VPRE; ++i)
@@ -456,8 +498,8 @@ void fa_fwd_bf16_kernel(Params p) {
 
   // Epilogue: O = acc / l (rounded to bf16 once), LSE = (m + log2 le) * ln 2.
   uint16_t* __restrict__ Oh =
-      (uint16_t*)p.o + (GEN ? b * p.obs + hh * p.ohs : (long long)hoff);
-  float* __restrict__ Lh = p.lse + (size_t)bh * N;
+      (uint16_t*)p.o + (GEN ? b * p.obs + hh * p.ohs + qr0 * p.ors : (long long)hoff);
+  float* __restrict__ Lh = p.lse + (VL ? hh * p.total_q + qr0 : (long long)bh * N);
   const float lt = pair_sum(l_run);
   const float le = pair_sum(le_run);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
@@ -622,9 +664,12 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(Params p) {
 // Host side
 // ---------------------------------------------------------------------------
 
+// Head dimensions of the bf16 forward kernels (the fp32 kernel: 64 and 128).
+bool bf16_head_dim(int d) { return d == 32 || d == 64 || d == 96 || d == 128; }
+
 int check_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
                int B, int H, int N, int d, float scale, int mask_kind, const int32_t* kv_lens,
-               int bm) {
+               int bm, bool bf16) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   const uintptr_t al = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse;
   if (al & 15u) return FA_ERR_INVALID_ARG;
@@ -632,7 +677,7 @@ int check_args(const void* q, const void* k, const void* v, const void* o, const
   if (mask_kind & ~(FA_MASK_CAUSAL | FA_MASK_KEY_PADDING)) return FA_ERR_INVALID_ARG;
   if ((mask_kind & FA_MASK_KEY_PADDING) && !kv_lens) return FA_ERR_INVALID_ARG;
   if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (bf16 ? !bf16_head_dim(d) : (d != 64 && d != 128)) return FA_ERR_UNSUPPORTED;
   const long long nqb = ((long long)N + bm - 1) / bm;
   if ((long long)B * H * nqb > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
   // One head's rows (plus one block of rows past the end) are addressed with
@@ -663,12 +708,28 @@ Params make_params(const void* q, const void* k, const void* v, void* o, float* 
 
 constexpr long long kCUs = 256;   // compute units of an MI355X
 
+// One bf16 forward launch: 8-wave (256-row) workgroups when big, else 4-wave.
+template <int MODE>
+void launch_bf16(int d, bool big, dim3 grid, hipStream_t s, const Params& p) {
+  const dim3 block(big ? 512 : 256);
+#define FA_LAUNCH(DD)                                                                   \
+  if (big) hipLaunchKernelGGL((fa_fwd_bf16_kernel<DD, 8, MODE>), grid, block, 0, s, p); \
+  else hipLaunchKernelGGL((fa_fwd_bf16_kernel<DD, 4, MODE>), grid, block, 0, s, p)
+  switch (d) {
+    case 32: FA_LAUNCH(32); break;
+    case 64: FA_LAUNCH(64); break;
+    case 96: FA_LAUNCH(96); break;
+    default: FA_LAUNCH(128); break;
+  }
+#undef FA_LAUNCH
+}
+
 }  // namespace
 
 extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                       int H, int N, int d, float scale, int mask_kind, const int32_t* kv_lens,
                       void* stream) {
-  const int st = check_args(q, k, v, o, lse, B, H, N, d, scale, mask_kind, kv_lens, 256);
+  const int st = check_args(q, k, v, o, lse, B, H, N, d, scale, mask_kind, kv_lens, 256, true);
   if (st != FA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   // 256-row workgroups (8 waves, one per CU) share each K/V tile among more
@@ -680,14 +741,7 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
   const int BM = big ? 256 : 128;
   const int nqb = (N + BM - 1) / BM;
   const Params p = make_params(q, k, v, o, lse, H, N, nqb, scale, mask_kind, kv_lens);
-  const dim3 grid((unsigned)(B * H * nqb)), block(big ? 512 : 256);
-  if (d == 128) {
-    if (big) hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, 8, false>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, 4, false>), grid, block, 0, s, p);
-  } else {
-    if (big) hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, 8, false>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, 4, false>), grid, block, 0, s, p);
-  }
+  launch_bf16<0>(d, big, dim3((unsigned)(B * H * nqb)), s, p);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -703,7 +757,7 @@ extern "C" int fa_fwd_general(const void* q, const void* k, const void* v, void*
   if (mask_kind & ~(FA_MASK_CAUSAL | FA_MASK_KEY_PADDING)) return FA_ERR_INVALID_ARG;
   if ((mask_kind & FA_MASK_KEY_PADDING) && !kv_lens) return FA_ERR_INVALID_ARG;
   if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (!bf16_head_dim(d)) return FA_ERR_UNSUPPORTED;
   // Strides (elements): NULL = contiguous [B, H, rows, d].  Rows must be
   // 16-byte aligned and hold d contiguous elements; batch and head starts
   // 16-byte aligned.
@@ -737,15 +791,47 @@ extern "C" int fa_fwd_general(const void* q, const void* k, const void* v, void*
   p.kbs = st[1][0]; p.khs = st[1][1]; p.krs = (unsigned)(st[1][2] * 2);
   p.vbs = st[2][0]; p.vhs = st[2][1]; p.vrs = (unsigned)(st[2][2] * 2);
   p.obs = st[3][0]; p.ohs = st[3][1]; p.ors = (unsigned)st[3][2];
-  const dim3 grid((unsigned)(B * H * nqb)), block(big ? 512 : 256);
-  hipStream_t s = (hipStream_t)stream;
-  if (d == 128) {
-    if (big) hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, 8, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((fa_fwd_bf16_kernel<128, 4, true>), grid, block, 0, s, p);
-  } else {
-    if (big) hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, 8, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((fa_fwd_bf16_kernel<64, 4, true>), grid, block, 0, s, p);
-  }
+  launch_bf16<1>(d, big, dim3((unsigned)(B * H * nqb)), (hipStream_t)stream, p);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B,
+                             int H, int d, int64_t total_q, int64_t total_k, int max_seqlen_q,
+                             float scale, int mask_kind, int window_left, void* stream) {
+  if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k) return FA_ERR_INVALID_ARG;
+  const uintptr_t al = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse;
+  if (al & 15u) return FA_ERR_INVALID_ARG;
+  if (((uintptr_t)cu_seqlens_q | (uintptr_t)cu_seqlens_k) & 3u) return FA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || window_left < -1)
+    return FA_ERR_INVALID_ARG;
+  if (mask_kind & ~FA_MASK_CAUSAL) return FA_ERR_INVALID_ARG;   // lengths come from cu_seqlens_k
+  if (!isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (!bf16_head_dim(d)) return FA_ERR_UNSUPPORTED;
+  if (max_seqlen_q == 0 || total_q == 0) return FA_OK;          // no query rows: nothing to write
+  if (max_seqlen_q > total_q) max_seqlen_q = (int)total_q;
+  // Packed rows are H*d elements apart; a sequence's rows (plus a block past
+  // the end) use 32-bit byte offsets.
+  const long long rowb = (long long)H * d * 2;
+  if ((total_q + 256) * rowb > 0xffffffffLL || (total_k + 256) * rowb > 0xffffffffLL)
+    return FA_ERR_INVALID_ARG;
+  const bool causal = (mask_kind & FA_MASK_CAUSAL) != 0;
+  const long long grid256 = (long long)B * H * ((max_seqlen_q + 255) / 256);
+  const bool big = grid256 >= (causal ? 2 : 1) * kCUs;
+  const int BM = big ? 256 : 128;
+  const int nqb = (max_seqlen_q + BM - 1) / BM;
+  if ((long long)B * H * nqb > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  Params p = make_params(q, k, v, o, lse, H, max_seqlen_q, nqb, scale, mask_kind, nullptr);
+  p.window = window_left;
+  p.qhs = d; p.qrs = (unsigned)rowb;
+  p.khs = d; p.krs = (unsigned)rowb;
+  p.vhs = d; p.vrs = (unsigned)rowb;
+  p.ohs = d; p.ors = (unsigned)(H * d);
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.total_q = total_q;
+  p.total_k = total_k;
+  launch_bf16<2>(d, big, dim3((unsigned)(B * H * nqb)), (hipStream_t)stream, p);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -753,7 +839,7 @@ extern "C" int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, 
                           int H, int N, int d, float scale, int mask_kind, const int32_t* kv_lens,
                           void* stream) {
   constexpr int BM = 32 * kWaves;
-  const int st = check_args(q, k, v, o, lse, B, H, N, d, scale, mask_kind, kv_lens, BM);
+  const int st = check_args(q, k, v, o, lse, B, H, N, d, scale, mask_kind, kv_lens, BM, false);
   if (st != FA_OK) return st;
   const int nqb = (N + BM - 1) / BM;
   const Params p = make_params(q, k, v, o, lse, H, N, nqb, scale, mask_kind, kv_lens);
@@ -770,7 +856,8 @@ extern "C" const char* fa_strerror(int status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_INVALID_ARG: return "invalid argument";
-    case FA_ERR_UNSUPPORTED: return "unsupported head dimension (d must be 64 or 128)";
+    case FA_ERR_UNSUPPORTED:
+      return "unsupported head dimension (bf16 forward: 32, 64, 96, 128; others: 64, 128)";
     case FA_ERR_HIP: return "HIP launch failure";
     default: return "unknown status";
   }

@@ -63,7 +63,9 @@ class Workload:
     kv_len_range: Optional[Tuple[int, int]] = None
     note: str = field(default="", compare=False)
     window_left: int = -1      # sliding window (general forward only)
-    layout: str = "bhnd"       # "bnhd": tensors stored [B, N, H, d] (general forward only)
+    layout: str = "bhnd"       # "bnhd": tensors stored [B, N, H, d] (general forward only);
+    #                            "varlen": B packed sequences, lengths U[len_range] (N = max)
+    len_range: Optional[Tuple[int, int]] = None
 
     @property
     def scale(self) -> float:
@@ -72,7 +74,13 @@ class Workload:
 
     def flops(self) -> float:
         """Forward FLOPs by the metric's formula: 4*B*H*N^2*d, halved when causal.
-        With a sliding window: 4*d per visible (query, key) pair."""
+        With a sliding window: 4*d per visible (query, key) pair.  Packed
+        sequences: the same count summed over the sequences (n^2, or
+        n(n+1)/2 causal)."""
+        if self.layout == "varlen":
+            n = packed_lengths(self).astype(np.float64)
+            pairs = n * (n + 1) / 2.0 if self.mask_kind & MASK_CAUSAL else n * n
+            return 4.0 * self.H * self.d * float(pairs.sum())
         if self.window_left >= 0:
             W, N = self.window_left, self.N
             if self.mask_kind & MASK_CAUSAL:
@@ -151,7 +159,20 @@ GENERAL_WORKLOADS = {
     "bf16_b2h32_n4096_d128_causal_bnhd": Workload(
         "bf16_b2h32_n4096_d128_causal_bnhd", 2, 32, 4096, 128, "bf16", MASK_CAUSAL, seed=3,
         q_mult=2.0, layout="bnhd", note="the bench workload stored [B, N, H, d]"),
+    "bf16_varlen_b16h32_n512_4096_d128_causal": Workload(
+        "bf16_varlen_b16h32_n512_4096_d128_causal", 16, 32, 4096, 128, "bf16", MASK_CAUSAL,
+        seed=8, q_mult=2.0, layout="varlen", len_range=(512, 4096),
+        note="16 packed causal sequences, lengths uniform in [512, 4096]"),
 }
+
+
+def packed_lengths(wl: "Workload") -> np.ndarray:
+    """The B sequence lengths of a packed workload (seeded, uniform in
+    ``len_range``; the longest is set to N so max_seqlen is exactly N)."""
+    lo, hi = wl.len_range
+    n = _streams(wl.seed)[3].integers(lo, hi, size=wl.B, endpoint=True).astype(np.int64)
+    n[int(np.argmax(n))] = wl.N
+    return n
 
 # The workload the throughput figure is quoted on.
 BENCH_WORKLOAD = "bf16_b2h32_n4096_d128_causal"
@@ -265,6 +286,27 @@ def make_raw(B: int, H: int, N: int, d: int, dtype: str, seed: int,
     return {"q": q, "k": k, "v": v, "kv_lens": kv_lens}
 
 
+def make_packed(lens_q, lens_k, H: int, d: int, seed: int, q_mult: float = 1.0):
+    """Packed variable-length bf16 inputs: q ``[total_q, H, d]``, k, v
+    ``[total_k, H, d]`` (bf16 bit patterns, N(0, 1) draws rounded to bf16,
+    q scaled by ``q_mult`` first) and the boundaries cu_q, cu_k (int32
+    ``[B + 1]``, cumulative lengths starting at 0)."""
+    lens_q = np.asarray(lens_q, dtype=np.int64)
+    lens_k = np.asarray(lens_k, dtype=np.int64)
+    if lens_q.shape != lens_k.shape or (lens_q < 0).any() or (lens_k < 0).any():
+        raise ValueError("lens_q and lens_k must be equally long lists of lengths >= 0")
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+    gq, gk, gv, _ = _streams(seed)
+    q = gq.standard_normal((int(cu_q[-1]), H, d), dtype=np.float32)
+    if q_mult != 1.0:
+        q *= np.float32(q_mult)
+    k = gk.standard_normal((int(cu_k[-1]), H, d), dtype=np.float32)
+    v = gv.standard_normal((int(cu_k[-1]), H, d), dtype=np.float32)
+    return {"q": f32_to_bf16_bits(q), "k": f32_to_bf16_bits(k), "v": f32_to_bf16_bits(v),
+            "cu_q": cu_q, "cu_k": cu_k}
+
+
 def make_grad_out(B: int, H: int, N: int, d: int, dtype: str, seed: int):
     """Draw the upstream gradient dO ``[B, H, N, d]`` for the backward pass."""
     if dtype not in ("f32", "bf16"):
@@ -309,6 +351,9 @@ def make_paged_decode(B: int, H: int, d: int, block_size: int, len_range, seed: 
 
 def make_inputs(wl: Workload):
     """Draw the inputs of a named workload (see ``WORKLOADS``)."""
+    if wl.layout == "varlen":
+        n = packed_lengths(wl)
+        return make_packed(n, n, wl.H, wl.d, wl.seed, q_mult=wl.q_mult)
     return make_raw(wl.B, wl.H, wl.N, wl.d, wl.dtype, wl.seed,
                     q_mult=wl.q_mult, kv_len_range=wl.kv_len_range)
 

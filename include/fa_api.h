@@ -26,8 +26,8 @@
  *  - lse: DEVICE pointer to float32 [B, H, N], natural-log units of the
  *    scaled logits.  A query row with no visible key gets O = 0 and
  *    LSE = -inf.
- *  - B, H, N >= 1; d is 64 or 128.  B * H * ceil(N / 128) must not exceed
- *    2^31 - 1.
+ *  - B, H, N >= 1; d is 32, 64, 96 or 128 for fa_fwd, 64 or 128 for
+ *    fa_fwd_f32.  B * H * ceil(N / 128) must not exceed 2^31 - 1.
  *  - scale: any finite float; the logits are scale * q.k.  (1/sqrt(d) is the
  *    usual value.)  |scale| below 1e-30 is treated as 1e-30, which gives the
  *    same uniform softmax as scale = 0 to within float32 rounding.
@@ -72,7 +72,7 @@ enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size, bad mask bits,
                               non-finite scale, padding without kv_lens */
-  FA_ERR_UNSUPPORTED = -2, /* head dimension d other than 64 or 128 */
+  FA_ERR_UNSUPPORTED = -2, /* head dimension the entry point does not support */
   FA_ERR_HIP = -3          /* the kernel launch failed */
 };
 
@@ -107,7 +107,7 @@ int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
  *    c < kv_len (key padding), c <= a_r (FA_MASK_CAUSAL), and
  *    c >= a_r - window_left when window_left >= 0 (window_left = -1: no
  *    window).  A row that sees no key gets O = 0, LSE = -inf.
- *  - Nq, Nk >= 1; d is 64 or 128; 16-byte aligned pointers; other
+ *  - Nq, Nk >= 1; d is 32, 64, 96 or 128; 16-byte aligned pointers; other
  *    conventions (scale, kv_lens, stream, errors) as for fa_fwd.  With
  *    contiguous strides, Nq = Nk and no window it computes exactly fa_fwd. */
 int fa_fwd_general(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -115,6 +115,30 @@ int fa_fwd_general(const void* q, const void* k, const void* v, void* o, float* 
                    const int64_t* k_strides, const int64_t* v_strides,
                    const int64_t* o_strides, float scale, int mask_kind, int window_left,
                    const int32_t* kv_lens, void* stream);
+
+/* Variable-length bf16 forward over packed sequences (the variable-length
+ * batches that "FlashAttention 完整解析" §11 lists for the library): B
+ * sequences of different lengths stored back to back, each attended on its
+ * own exactly as fa_fwd_general attends one batch entry.
+ *  - q, o: DEVICE bf16 [total_q, H, d]; k, v: DEVICE bf16 [total_k, H, d],
+ *    contiguous, 16-byte aligned.  lse: DEVICE float32 [H, total_q].
+ *  - cu_seqlens_q, cu_seqlens_k: DEVICE int32 [B + 1], non-decreasing,
+ *    starting at 0: sequence b owns query rows cu_seqlens_q[b] ..
+ *    cu_seqlens_q[b+1] - 1 and key rows cu_seqlens_k[b] .. cu_seqlens_k[b+1]
+ *    - 1.  Its Nq_b queries sit at the last Nq_b of its Nk_b key positions;
+ *    causal and window_left act as in fa_fwd_general within the sequence.
+ *    The values are not read on the host: each is clamped into [0, total]
+ *    on the device, so bad values cannot reach outside the tensors (the
+ *    result is then meaningless, and overlapping sequences race).
+ *  - max_seqlen_q must be at least every Nq_b: rows past it are not
+ *    written.  mask_kind: FA_MASK_NONE or FA_MASK_CAUSAL (key lengths come
+ *    from cu_seqlens_k).  A sequence with Nk_b = 0 gets O = 0, LSE = -inf.
+ *  - total_q = 0 or max_seqlen_q = 0 enqueues nothing.  Other conventions
+ *    (d, scale, stream, errors) as for fa_fwd_general. */
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B, int H,
+                  int d, int64_t total_q, int64_t total_k, int max_seqlen_q, float scale,
+                  int mask_kind, int window_left, void* stream);
 
 /* FP8 forward (the FP8 path of "FlashAttention 完整解析" §5.5 and of the
  * youngju.dev walkthrough §9.2): q, k, v hold OCP FP8 E4M3 codes

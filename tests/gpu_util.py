@@ -145,3 +145,28 @@ def compare_grads(g, ref, mag, what="", keys=("dq", "dk", "dv"), bulk=False):
     say(f"  {what}: " + " ".join(f"{n}: relF={a:.2e} err/bound={b:.2f}"
                                  for n, (a, b) in stats.items()))
     return stats
+
+
+def compare_bound(O, L, ref, what):
+    """Element-wise parity of a bf16 forward with probabilities rounded to
+    bf16: |err| <= 2^-8 |O_ref| (O's own rounding) + (2^-7 + 1e-5) (P|V|)
+    (P rounded to bf16 and normalised by the sum of the rounded values, fp32
+    sums), relative Frobenius <= 5e-3, LSE within 1e-3; rows without a
+    visible key exactly O = 0, LSE = -inf; no unwritten (NaN) element.
+    ``ref`` is (O_ref, LSE_ref, P|V|) from the oracle's ``magnitudes``; O is
+    laid out as LSE's rows followed by d."""
+    Or, Lr, M = ref
+    assert not np.isnan(O).any() and not np.isnan(L).any(), f"{what}: unwritten elements"
+    empty = ~np.isfinite(Lr)
+    assert np.array_equal(~np.isfinite(L), empty), f"{what}: LSE -inf pattern"
+    assert np.all(O[empty] == 0.0) and np.all(L[empty] == -np.inf), f"{what}: empty rows"
+    err = np.abs(O - Or)
+    bound = 2.0 ** -8 * np.abs(Or) + (2.0 ** -7 + 1e-5) * M
+    zero = bound == 0
+    assert np.all(err[zero] == 0.0), what
+    ratio = float(np.max(err[~zero] / bound[~zero], initial=0.0))
+    nrm = np.linalg.norm(Or)
+    relf = float(np.linalg.norm(O - Or) / nrm) if nrm > 0 else 0.0
+    lerr = float(np.abs(L[~empty] - Lr[~empty]).max(initial=0.0))
+    say(f"  {what}: err/bound={ratio:.2f} relF={relf:.2e} max|dLSE|={lerr:.2e}")
+    assert ratio <= 1.0 and relf <= 5e-3 and lerr <= 1e-3, (what, ratio, relf, lerr)

@@ -28,7 +28,7 @@ def lib():
 def test_header_declares_the_entry_points():
     assert _declared() == ["fa_bwd", "fa_decode_paged", "fa_decode_paged_workspace_bytes",
                            "fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_fwd_general",
-                           "fa_strerror"]
+                           "fa_fwd_varlen", "fa_strerror"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -68,8 +68,11 @@ def test_invalid_arguments_are_rejected_before_launch(lib, name):
     assert _call(lib, name, scale=float("nan")) == bad
     assert _call(lib, name, scale=float("inf")) == bad
     assert _call(lib, name, B=1 << 20, H=1 << 10, N=1 << 20) == bad  # grid too large
-    assert _call(lib, name, d=96) == fa.FA_ERR_UNSUPPORTED
+    if name == "fa_fwd_f32":
+        assert _call(lib, name, d=96) == fa.FA_ERR_UNSUPPORTED
+        assert _call(lib, name, d=32) == fa.FA_ERR_UNSUPPORTED
     assert _call(lib, name, d=256) == fa.FA_ERR_UNSUPPORTED
+    assert _call(lib, name, d=48) == fa.FA_ERR_UNSUPPORTED
 
 
 def _bwd(lib, ptrs=None, B=1, H=1, N=16, d=64, scale=0.125, mask=0, kv=None):
@@ -171,7 +174,30 @@ def test_general_invalid_arguments_are_rejected_before_launch(lib):
     assert call(strides=(st(0, 0, 32), None, None, None)) == bad        # row stride < d
     assert call(strides=(st(0, 3, 64), None, None, None)) == bad        # misaligned head stride
     assert call(strides=(None, st(0, 0, 1 << 40), None, None)) == bad   # rows beyond 32-bit offsets
-    assert call(d=96) == fa.FA_ERR_UNSUPPORTED
+    assert call(d=256) == fa.FA_ERR_UNSUPPORTED and call(d=80) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_varlen_invalid_arguments_are_rejected_before_launch(lib):
+    import exact_attention_92_amd as fa
+    bad = fa.FA_ERR_INVALID_ARG
+    good = [0x1000 * (i + 1) for i in range(7)]
+
+    def call(ptrs=good, B=2, H=2, d=64, tq=100, tk=120, maxq=60, scale=0.1, mask=0, window=-1):
+        return lib.fa_fwd_varlen(*[ctypes.c_void_p(p) if p is not None else None for p in ptrs],
+                                 B, H, d, tq, tk, maxq, ctypes.c_float(scale), mask, window, None)
+    for i in range(7):
+        p = list(good)
+        p[i] = None
+        assert call(p) == bad
+        p[i] = good[i] + (2 if i >= 5 else 8)     # cu_seqlens need 4 bytes, tensors 16
+        assert call(p) == bad
+    assert call(B=0) == bad and call(H=0) == bad and call(tq=-1) == bad and call(tk=-1) == bad
+    assert call(maxq=-1) == bad and call(window=-2) == bad and call(scale=float("inf")) == bad
+    assert call(mask=fa.FA_MASK_KEY_PADDING) == bad and call(mask=4) == bad
+    assert call(tq=1 << 31, H=64, d=128) == bad                     # rows beyond 32-bit offsets
+    assert call(d=256) == fa.FA_ERR_UNSUPPORTED
+    # Nothing to compute: succeeds without touching the (fake) pointers.
+    assert call(tq=0) == fa.FA_OK and call(maxq=0) == fa.FA_OK
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

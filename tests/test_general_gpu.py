@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 
 from fa_inputs import MASK_CAUSAL, MASK_KEY_PADDING, MASK_NONE, make_raw, to_f64
+from gpu_util import compare_bound as compare
 from gpu_util import o_to_f64, say, to_dev
 from oracle import attention_general_ref
 
@@ -63,24 +64,6 @@ def run_general(x, scale, mask, window, layout="bhnd"):
 def oracle(x, scale, mask, window):
     return attention_general_ref(to_f64(x["q"]), to_f64(x["k"]), to_f64(x["v"]), scale, mask,
                                  window, x.get("kv_lens"), magnitudes=True)
-
-
-def compare(O, L, ref, what):
-    Or, Lr, M = ref
-    assert not np.isnan(O).any() and not np.isnan(L).any(), f"{what}: unwritten elements"
-    empty = ~np.isfinite(Lr)
-    assert np.array_equal(~np.isfinite(L), empty), f"{what}: LSE -inf pattern"
-    assert np.all(O[empty] == 0.0) and np.all(L[empty] == -np.inf), f"{what}: empty rows"
-    err = np.abs(O - Or)
-    bound = 2.0 ** -8 * np.abs(Or) + (2.0 ** -7 + 1e-5) * M
-    zero = bound == 0
-    assert np.all(err[zero] == 0.0), what
-    ratio = float(np.max(err[~zero] / bound[~zero], initial=0.0))
-    nrm = np.linalg.norm(Or)
-    relf = float(np.linalg.norm(O - Or) / nrm) if nrm > 0 else 0.0
-    lerr = float(np.abs(L[~empty] - Lr[~empty]).max(initial=0.0))
-    say(f"  {what}: err/bound={ratio:.2f} relF={relf:.2e} max|dLSE|={lerr:.2e}")
-    assert ratio <= 1.0 and relf <= 5e-3 and lerr <= 1e-3, (what, ratio, relf, lerr)
 
 
 @pytest.mark.parametrize("d", [64, 128])

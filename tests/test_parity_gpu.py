@@ -182,7 +182,7 @@ def test_errors_write_nothing():
     import torch
 
     import exact_attention_92_amd as fa
-    q = torch.zeros((1, 1, 64, 96), dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros((1, 1, 64, 80), dtype=torch.bfloat16, device="cuda")
     o = torch.full_like(q, float("nan"))
     lse = torch.full((1, 1, 64), float("nan"), device="cuda")
     with pytest.raises(fa.FaError) as e:
