@@ -226,8 +226,10 @@ struct Params {
 // the queries at the last N_q key positions, sliding window, arbitrary
 // batch/head/row strides.  MODE 2 (varlen): MODE 1 over packed sequences
 // whose boundaries are read from cu_q / cu_k.
+// d = 256 needs about 300 live registers: one wave per SIMD.
 template <int D, int NW, int MODE>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(FA_WAVES_PER_EU)))
+__global__ __launch_bounds__(64 * NW)
+__attribute__((amdgpu_waves_per_eu(D > 128 ? 1 : FA_WAVES_PER_EU)))
 void fa_fwd_bf16_kernel(Params p) {
   constexpr bool GEN = MODE != 0;
   constexpr bool VL = MODE == 2;
@@ -246,7 +248,8 @@ void fa_fwd_bf16_kernel(Params p) {
   constexpr int KU = (KUNITS + kThreads - 1) / kThreads;   // per thread
   constexpr bool KFULL = KUNITS % kThreads == 0;           // every thread has KU pieces
   constexpr int VUNITS = (BN / 4) * CPR;     // V pieces of 4 keys x 8 dims
-  static_assert(D % 32 == 0 && VUNITS <= kThreads, "tile shape");
+  constexpr int VU = (VUNITS + kThreads - 1) / kThreads;   // per thread
+  static_assert(D % 32 == 0, "tile shape");
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][BN][KLD];
   __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][D][VLD];
@@ -325,19 +328,30 @@ void fa_fwd_bf16_kernel(Params p) {
     k_off[u] = (KFULL || unit < KUNITS) ? (uint32_t)(unit / CPR) * KRB + 16u * (unit % CPR)
                                         : 0x80000000u;
   }
-  const bool v_unit = tid < VUNITS;   // VUNITS <= kThreads: one piece per thread at most
-  const int vkg = tid % (BN / 4), vdc = tid / (BN / 4);
-  const uint32_t v_off = (uint32_t)(4 * vkg) * VRB + 16u * vdc;
-  u32x4_t kreg[KU], vreg[4];
+  bool v_unit[VU];
+  int vkg[VU], vdc[VU];
+  uint32_t v_off[VU];
+#pragma unroll
+  for (int u = 0; u < VU; ++u) {
+    const int unit = tid + u * kThreads;
+    v_unit[u] = unit < VUNITS;
+    vkg[u] = unit % (BN / 4);
+    vdc[u] = unit / (BN / 4);
+    v_off[u] = (uint32_t)(4 * vkg[u]) * VRB + 16u * vdc[u];
+  }
+  u32x4_t kreg[KU], vreg[VU][4];
   auto load_block = [&](int j) {
     const int kbase = j * BN;
     const rsrc_t rk = make_rsrc(Kh + (size_t)kbase * (KRB / 2), (uint32_t)max(0, Nk - kbase) * KRB);
     const rsrc_t rv = make_rsrc(Vh + (size_t)kbase * (VRB / 2), (uint32_t)max(0, n_vis - kbase) * VRB);
 #pragma unroll
     for (int u = 0; u < KU; ++u) kreg[u] = buf_load16(rk, k_off[u]);
-    if (v_unit) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vreg[i] = buf_load16(rv, v_off + i * VRB);
+    for (int u = 0; u < VU; ++u) {
+      if (v_unit[u]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vreg[u][i] = buf_load16(rv, v_off[u] + i * VRB);
+      }
     }
   };
   auto store_block = [&](int buf) {
@@ -346,18 +360,22 @@ void fa_fwd_bf16_kernel(Params p) {
       const int unit = tid + u * kThreads;
       if (KFULL || unit < KUNITS) *(u32x4_t*)&k_lds[buf][unit / CPR][8 * (unit % CPR)] = kreg[u];
     }
-    if (v_unit) {
-      // Dword w of key i holds dims 8*vdc + 2w, +1: regroup into
-      // (keys 0-3 of dim 2w) and (keys 0-3 of dim 2w+1).
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const unsigned a0 = vreg[0][w], a1 = vreg[1][w], a2 = vreg[2][w], a3 = vreg[3][w];
-        const u32x2_t lo = {__builtin_amdgcn_perm(a1, a0, 0x05040100u),
-                            __builtin_amdgcn_perm(a3, a2, 0x05040100u)};
-        const u32x2_t hi = {__builtin_amdgcn_perm(a1, a0, 0x07060302u),
-                            __builtin_amdgcn_perm(a3, a2, 0x07060302u)};
-        *(u32x2_t*)&vt_lds[buf][8 * vdc + 2 * w][4 * vkg] = lo;
-        *(u32x2_t*)&vt_lds[buf][8 * vdc + 2 * w + 1][4 * vkg] = hi;
+    for (int u = 0; u < VU; ++u) {
+      if (v_unit[u]) {
+        // Dword w of key i holds dims 8*vdc + 2w, +1: regroup into
+        // (keys 0-3 of dim 2w) and (keys 0-3 of dim 2w+1).
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const unsigned a0 = vreg[u][0][w], a1 = vreg[u][1][w], a2 = vreg[u][2][w],
+                         a3 = vreg[u][3][w];
+          const u32x2_t lo = {__builtin_amdgcn_perm(a1, a0, 0x05040100u),
+                              __builtin_amdgcn_perm(a3, a2, 0x05040100u)};
+          const u32x2_t hi = {__builtin_amdgcn_perm(a1, a0, 0x07060302u),
+                              __builtin_amdgcn_perm(a3, a2, 0x07060302u)};
+          *(u32x2_t*)&vt_lds[buf][8 * vdc[u] + 2 * w][4 * vkg[u]] = lo;
+          *(u32x2_t*)&vt_lds[buf][8 * vdc[u] + 2 * w + 1][4 * vkg[u]] = hi;
+        }
       }
     }
   };
@@ -665,7 +683,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(Params p) {
 // ---------------------------------------------------------------------------
 
 // Head dimensions of the bf16 forward kernels (the fp32 kernel: 64 and 128).
-bool bf16_head_dim(int d) { return d == 32 || d == 64 || d == 96 || d == 128; }
+bool bf16_head_dim(int d) { return d == 32 || d == 64 || d == 96 || d == 128 || d == 256; }
 
 int check_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
                int B, int H, int N, int d, float scale, int mask_kind, const int32_t* kv_lens,
@@ -719,7 +737,10 @@ void launch_bf16(int d, bool big, dim3 grid, hipStream_t s, const Params& p) {
     case 32: FA_LAUNCH(32); break;
     case 64: FA_LAUNCH(64); break;
     case 96: FA_LAUNCH(96); break;
-    default: FA_LAUNCH(128); break;
+    case 128: FA_LAUNCH(128); break;
+    default:   // 256: 4-wave (128-row) workgroups only, one wave per SIMD
+      hipLaunchKernelGGL((fa_fwd_bf16_kernel<256, 4, MODE>), grid, block, 0, s, p);
+      break;
   }
 #undef FA_LAUNCH
 }
@@ -737,7 +758,7 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
   // causal masks, whose query blocks differ in cost); otherwise 128-row
   // workgroups (two per CU) balance better.
   const long long grid256 = (long long)B * H * ((N + 255) / 256);
-  const bool big = grid256 >= ((mask_kind & FA_MASK_CAUSAL) ? 2 : 1) * kCUs;
+  const bool big = d != 256 && grid256 >= ((mask_kind & FA_MASK_CAUSAL) ? 2 : 1) * kCUs;
   const int BM = big ? 256 : 128;
   const int nqb = (N + BM - 1) / BM;
   const Params p = make_params(q, k, v, o, lse, H, N, nqb, scale, mask_kind, kv_lens);
@@ -779,7 +800,7 @@ extern "C" int fa_fwd_general(const void* q, const void* k, const void* v, void*
   }
   const bool causal = (mask_kind & FA_MASK_CAUSAL) != 0;
   const long long grid256 = (long long)B * H * ((Nq + 255) / 256);
-  const bool big = grid256 >= (causal ? 2 : 1) * kCUs;
+  const bool big = d != 256 && grid256 >= (causal ? 2 : 1) * kCUs;
   const int BM = big ? 256 : 128;
   const int nqb = (Nq + BM - 1) / BM;
   if ((long long)B * H * nqb > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
@@ -817,7 +838,7 @@ extern "C" int fa_fwd_varlen(const void* q, const void* k, const void* v, void* 
     return FA_ERR_INVALID_ARG;
   const bool causal = (mask_kind & FA_MASK_CAUSAL) != 0;
   const long long grid256 = (long long)B * H * ((max_seqlen_q + 255) / 256);
-  const bool big = grid256 >= (causal ? 2 : 1) * kCUs;
+  const bool big = d != 256 && grid256 >= (causal ? 2 : 1) * kCUs;
   const int BM = big ? 256 : 128;
   const int nqb = (max_seqlen_q + BM - 1) / BM;
   if ((long long)B * H * nqb > 0x7fffffffLL) return FA_ERR_INVALID_ARG;

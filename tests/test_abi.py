@@ -71,7 +71,9 @@ def test_invalid_arguments_are_rejected_before_launch(lib, name):
     if name == "fa_fwd_f32":
         assert _call(lib, name, d=96) == fa.FA_ERR_UNSUPPORTED
         assert _call(lib, name, d=32) == fa.FA_ERR_UNSUPPORTED
-    assert _call(lib, name, d=256) == fa.FA_ERR_UNSUPPORTED
+    if name == "fa_fwd_f32":
+        assert _call(lib, name, d=256) == fa.FA_ERR_UNSUPPORTED
+    assert _call(lib, name, d=512) == fa.FA_ERR_UNSUPPORTED
     assert _call(lib, name, d=48) == fa.FA_ERR_UNSUPPORTED
 
 
@@ -174,7 +176,7 @@ def test_general_invalid_arguments_are_rejected_before_launch(lib):
     assert call(strides=(st(0, 0, 32), None, None, None)) == bad        # row stride < d
     assert call(strides=(st(0, 3, 64), None, None, None)) == bad        # misaligned head stride
     assert call(strides=(None, st(0, 0, 1 << 40), None, None)) == bad   # rows beyond 32-bit offsets
-    assert call(d=256) == fa.FA_ERR_UNSUPPORTED and call(d=80) == fa.FA_ERR_UNSUPPORTED
+    assert call(d=512) == fa.FA_ERR_UNSUPPORTED and call(d=80) == fa.FA_ERR_UNSUPPORTED
 
 
 def test_varlen_invalid_arguments_are_rejected_before_launch(lib):
@@ -195,7 +197,7 @@ def test_varlen_invalid_arguments_are_rejected_before_launch(lib):
     assert call(maxq=-1) == bad and call(window=-2) == bad and call(scale=float("inf")) == bad
     assert call(mask=fa.FA_MASK_KEY_PADDING) == bad and call(mask=4) == bad
     assert call(tq=1 << 31, H=64, d=128) == bad                     # rows beyond 32-bit offsets
-    assert call(d=256) == fa.FA_ERR_UNSUPPORTED
+    assert call(d=512) == fa.FA_ERR_UNSUPPORTED and call(d=160) == fa.FA_ERR_UNSUPPORTED
     # Nothing to compute: succeeds without touching the (fake) pointers.
     assert call(tq=0) == fa.FA_OK and call(maxq=0) == fa.FA_OK
 

@@ -1,5 +1,5 @@
 """GPU parity of the packed variable-length forward (fa_fwd_varlen) and of
-the head dimensions 32 and 96 (fa_fwd, fa_fwd_general), against the
+the head dimensions 32, 96 and 256 (fa_fwd, fa_fwd_general), against the
 oracle, with the element bound of the general forward (O's bf16 rounding
 plus P rounded to bf16, see gpu_util.compare_bound).  Outputs are
 pre-filled with NaN so an unwritten element fails."""
@@ -52,7 +52,7 @@ LENS = ([0, 1, 63, 64, 65, 200, 257, 10, 300],      # queries per sequence
         [5, 1, 63, 100, 65, 129, 257, 0, 1000])    # keys per sequence (10 queries, no keys)
 
 
-@pytest.mark.parametrize("d", [32, 64, 96, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
 def test_ragged_packing(d):
     x = make_packed(*LENS, H=3, d=d, seed=200 + d, q_mult=2.0)
     for mask in (MASK_NONE, MASK_CAUSAL):
@@ -100,8 +100,8 @@ def test_rows_past_max_seqlen_are_not_written():
     assert np.abs(O[ok] - Or[ok]).max() <= 1e-2 and np.abs(L[:, ok] - Lr[:, ok]).max() <= 1e-3
 
 
-@pytest.mark.parametrize("d", [32, 96])
-def test_head_dims_32_96_self_attention(d):
+@pytest.mark.parametrize("d", [32, 96, 256])
+def test_extra_head_dims_self_attention(d):
     import torch
 
     import exact_attention_92_amd as fa
@@ -120,8 +120,8 @@ def test_head_dims_32_96_self_attention(d):
                           f"fa_fwd d={d} N={N} mask={mask}")
 
 
-@pytest.mark.parametrize("d", [32, 96])
-def test_head_dims_32_96_general(d):
+@pytest.mark.parametrize("d", [32, 96, 256])
+def test_extra_head_dims_general(d):
     import torch
 
     import exact_attention_92_amd as fa
@@ -161,3 +161,24 @@ def test_varlen_bench_workload_sampled_sequences():
                                                          ref[2].transpose(t)),
                       f"{wl.name} sequence {s_} (n={sub_cu[1]})")
     assert not np.isnan(O).any() and not np.isnan(L).any()
+
+
+def test_head_dim_256_long_causal_sampled_rows():
+    """d = 256 at N = 8192 (64 key blocks per row block), sampled rows."""
+    import torch
+
+    import exact_attention_92_amd as fa
+    B, H, N, d = 1, 4, 8192, 256
+    x = make_raw(B, H, N, d, "bf16", seed=260, q_mult=2.0)
+    say(f"[d=256] N={N} causal")
+    q, k, v = (to_dev(x[t]) for t in "qkv")
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((B, H, N), float("nan"), device="cuda")
+    fa.fa_fwd(q, k, v, o, lse, d ** -0.5, MASK_CAUSAL)
+    torch.cuda.synchronize()
+    O, L = o_to_f64(o), lse.cpu().numpy().astype(np.float64)
+    rows = np.unique(np.r_[0:40, np.linspace(0, N - 1, 40).astype(int), N - 40:N])
+    ref = attention_general_ref(to_f64(x["q"]), to_f64(x["k"]), to_f64(x["v"]), d ** -0.5,
+                                MASK_CAUSAL, -1, magnitudes=True, rows=rows)
+    assert not np.isnan(O).any() and not np.isnan(L).any()
+    compare_bound(O[:, :, rows], L[:, :, rows], ref, f"d=256 N={N} causal sampled")
