@@ -55,6 +55,10 @@
 //    is remapped so that consecutive work items of one head land on one XCD
 //    (shared L2 for that head's K/V), and causal query blocks run heaviest
 //    first.
+//  * One kernel template serves three entry points: contiguous
+//    self-attention (fa_fwd), the general layout with N_q != N_k, a sliding
+//    window and arbitrary strides (fa_fwd_general), and packed sequences of
+//    different lengths (fa_fwd_varlen); head dimensions 32 to 256.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -143,7 +147,7 @@ __device__ __forceinline__ void mfma_read_ahead() {
 }
 
 #ifndef FA_HEAD_GROUP
-#define FA_HEAD_GROUP 2
+#define FA_HEAD_GROUP 4
 #endif
 // Maps the linear workgroup id to (head, query block).  Workgroups are
 // dispatched round-robin over the 8 XCDs (w % 8), and in order within one.
