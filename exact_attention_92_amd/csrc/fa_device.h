@@ -89,16 +89,20 @@ __device__ __forceinline__ void transpose4x8(const u32x4_t (&x)[4], u32x2_t (&ou
 // Workgroups are dispatched round-robin over the 8 XCDs (w % 8), in order
 // within one.  Maps the linear workgroup id to (head, block) so that when the
 // heads split evenly XCD x owns a contiguous range of heads (their tensors
-// share its L2) and visits their blocks rank by rank, two heads at a time;
+// share its L2) and visits their blocks rank by rank, FA_WORK_GROUP (four)
+// heads at a time;
 // rank 0 is block nb-1 when heavy_last, else block 0.  Otherwise XCD x gets
 // the contiguous logical range [x*G/8, (x+1)*G/8).
+#ifndef FA_WORK_GROUP
+#define FA_WORK_GROUP 4
+#endif
 __device__ __forceinline__ void map_work(int nb, bool heavy_last, int& bh, int& blk) {
   const int G = gridDim.x;
   const int w = blockIdx.x;
   const int BH = G / nb;
   if (G % 8 == 0 && BH % 8 == 0) {
     const int hx = BH / 8, i = w / 8;
-    const int g = (hx % 2 == 0) ? 2 : hx;
+    const int g = (hx % FA_WORK_GROUP == 0) ? FA_WORK_GROUP : hx;
     const int grp = i / (g * nb), j = i - grp * (g * nb);
     bh = (w % 8) * hx + grp * g + j % g;
     const int r = j / g;
