@@ -19,9 +19,12 @@
 //    hold 32 keys in a fixed order; V^T is stored in LDS with its keys in
 //    that same order, so the rounded probabilities are directly the B
 //    operand of O^T = V^T P^T (two 16-byte LDS reads per operand).
-//  * The row max is exact (updated every block), so every probability is at
-//    most 1; P is scaled by 448 (the largest E4M3 value) before rounding --
-//    folded into the exponent -- which keeps values down to ~4e-6
+//  * The reference for the exponentials is the row max, moved only when a
+//    block's max exceeds it by more than kHeadroom (log2 units), so every
+//    probability is at most 2^kHeadroom and most blocks skip the rescaling of
+//    the state (any reference gives the same softmax).  P is scaled by
+//    448 / 2^kHeadroom (448 is the largest E4M3 value) before rounding --
+//    folded into the exponent -- which keeps values down to ~2e-5
 //    representable.  The factor and the V scale are divided out once in the
 //    epilogue; the row sum is the fp32 sum of the unrounded scaled
 //    probabilities (it also gives LSE).
@@ -42,6 +45,12 @@ typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 // log2(448); 448 is the largest finite E4M3 value.
 constexpr float kLog2P8Scale = 8.807354922057604f;
+// Probabilities may exceed 1 by up to 2^kHeadroom before the reference moves.
+#ifndef FA_FP8_HEADROOM
+#define FA_FP8_HEADROOM 2
+#endif
+constexpr float kHeadroom = (float)FA_FP8_HEADROOM;
+constexpr float kLog2PScale = kLog2P8Scale - kHeadroom;   // log2(448 / 2^kHeadroom)
 
 // D = A B + C, 32x32 tile, 64-deep E4M3 contraction, fp32 accumulation.
 // Lane l supplies A row / B column l%32, 32 contraction elements per lane
@@ -240,14 +249,16 @@ void fa_fwd_fp8_kernel(P8Params p) {
           for (int r = 0; r < 16; ++r)
             if (32 * kt + 16 * (r >> 3) + (r & 7) > lim) s[kt][r] = -INFINITY;
       }
-      // Exact running max; rescale the state when it moves.
+      // Block row max; the reference moves to it (and the state is rescaled)
+      // only when some row's max exceeds its reference by more than
+      // kHeadroom, or the reference is still -inf.
       float mx = s[0][0];
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
       const float m_new = fmaxf(m_run, pair_max(mx) * c);
-      if (__any(m_new != m_run)) {
+      if (__any(m_new > m_run + kHeadroom)) {
         const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
@@ -256,10 +267,10 @@ void fa_fwd_fp8_kernel(P8Params p) {
         l_run *= alpha;
         m_run = m_new;
       }
-      // e = 448 p = 2^(s c - m + log2 448) <= 448 (p <= 1); the P^T operand
-      // holds e rounded to E4M3, byte 16kt + r of the lane's 32 = register r
-      // of tile kt.  The row sum accumulates e, i.e. 448 times the sum of p.
-      const float base = ((m_run == -INFINITY) ? 0.f : m_run) - kLog2P8Scale;
+      // e = p 448 / 2^kHeadroom = 2^(s c - m + kLog2PScale) <= 448 (p <=
+      // 2^kHeadroom); the P^T operand holds e rounded to E4M3, byte 16kt + r
+      // of the lane's 32 = register r of tile kt.  The row sum accumulates e.
+      const float base = ((m_run == -INFINITY) ? 0.f : m_run) - kLog2PScale;
       i32x8_t pb;
       float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
@@ -286,7 +297,8 @@ void fa_fwd_fp8_kernel(P8Params p) {
     __syncthreads();
   }
 
-  // Epilogue (l_run holds 448 times the row sum): O = acc * v_descale / l_run,
+  // Epilogue (l_run holds 448 / 2^kHeadroom times the row sum relative to the
+  // reference): O = acc * v_descale / l_run,
   // rounded to bf16 once; LSE = (m + log2(l_run) - log2 448) ln 2.
   uint16_t* __restrict__ Oh = (uint16_t*)p.o + hoff;
   float* __restrict__ Lh = p.lse + (size_t)bh * N;
@@ -303,7 +315,7 @@ void fa_fwd_fp8_kernel(P8Params p) {
         *(u32x2_t*)(orow + 32 * dt + 8 * a + 4 * hf) = x;
       }
     if (hf == 0)
-      Lh[qrow] = lt > 0.f ? (m_run + __builtin_amdgcn_logf(lt) - kLog2P8Scale) * kLn2 : -INFINITY;
+      Lh[qrow] = lt > 0.f ? (m_run + __builtin_amdgcn_logf(lt) - kLog2PScale) * kLn2 : -INFINITY;
   }
 }
 

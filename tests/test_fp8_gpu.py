@@ -12,11 +12,12 @@ head dimension t:
   2^-11 |scale| |q_r|_2 max_c |k_c|_2 (Cauchy-Schwarz).  That moves every
   p_rc and the row sum by a factor within e^(+-g_r), so O by at most
   (e^(2 g_r) - 1) (P |V|)_rt, and LSE by at most g_r.
-* P.  448 p (p <= 1: the row max is exact) is rounded to E4M3: relative
+* P.  The kernel's reference max lags the row max by at most 2^2 (binary
+  orders of headroom, so p <= 4), and 448 p / 4 is rounded to E4M3: relative
   error at most 2^-4 for normal values, absolute at most 2^-10 (half the
-  smallest subnormal step) below 2^-6; the normalisation divides by the
-  fp32 sum of the unrounded p.  Summed over the visible keys this gives
-  2^-4 (P |V|)_rt + 2^-10/448 (sum_J |v_t|)_r / l_r.
+  smallest subnormal step) below 2^-6, i.e. 2^-10 * 4 / 448 in p; the
+  normalisation divides by the fp32 sum of the unrounded p.  Summed over the
+  visible keys this gives 2^-4 (P |V|)_rt + 2^-8/448 (sum_J |v_t|)_r / l_r.
 * O's own bf16 rounding: 2^-8 |O_ref|; fp32 sums and exp2: 1e-5 (P |V|).
 
 LSE: the logit term plus 1e-3 (the bf16 path's bar for its fp32 sums).
@@ -34,7 +35,7 @@ from oracle import attention_ref
 pytestmark = pytest.mark.gpu
 
 MASKS = [MASK_NONE, MASK_CAUSAL, MASK_KEY_PADDING, MASK_CAUSAL | MASK_KEY_PADDING]
-U8, SUB, U16, NOISE = 2.0 ** -4, 2.0 ** -10 / 448.0, 2.0 ** -8, 1e-5
+U8, SUB, U16, NOISE = 2.0 ** -4, 2.0 ** -10 * 4 / 448.0, 2.0 ** -8, 1e-5
 ACC = 2.0 ** -11     # accumulation error of the E4M3 matrix cores, per |term|
 
 
@@ -146,7 +147,7 @@ def test_unusual_scales(scale):
 
 
 def test_q_zero_closed_form_long_causal():
-    """Q = 0: every probability is exactly 1 (448 is exact in E4M3), so O_r is
+    """Q = 0: every probability is exactly 1 (448 / 4 is exact in E4M3), so O_r is
     the mean of the visible V rows up to bf16 rounding, at N = 65536."""
     B, H, N, d = 1, 2, 65536, 128
     say(f"[fp8 closed form] Q=0 causal N={N}")
