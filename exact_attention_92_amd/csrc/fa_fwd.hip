@@ -882,7 +882,7 @@ extern "C" const char* fa_strerror(int status) {
     case FA_OK: return "ok";
     case FA_ERR_INVALID_ARG: return "invalid argument";
     case FA_ERR_UNSUPPORTED:
-      return "unsupported head dimension (bf16 forward: 32, 64, 96, 128; others: 64, 128)";
+      return "unsupported head dimension (bf16 forward: 32, 64, 96, 128, 256; others: 64, 128)";
     case FA_ERR_HIP: return "HIP launch failure";
     default: return "unknown status";
   }

@@ -26,7 +26,7 @@
  *  - lse: DEVICE pointer to float32 [B, H, N], natural-log units of the
  *    scaled logits.  A query row with no visible key gets O = 0 and
  *    LSE = -inf.
- *  - B, H, N >= 1; d is 32, 64, 96 or 128 for fa_fwd, 64 or 128 for
+ *  - B, H, N >= 1; d is 32, 64, 96, 128 or 256 for fa_fwd, 64 or 128 for
  *    fa_fwd_f32.  B * H * ceil(N / 128) must not exceed 2^31 - 1.
  *  - scale: any finite float; the logits are scale * q.k.  (1/sqrt(d) is the
  *    usual value.)  |scale| below 1e-30 is treated as 1e-30, which gives the
@@ -107,7 +107,7 @@ int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
  *    c < kv_len (key padding), c <= a_r (FA_MASK_CAUSAL), and
  *    c >= a_r - window_left when window_left >= 0 (window_left = -1: no
  *    window).  A row that sees no key gets O = 0, LSE = -inf.
- *  - Nq, Nk >= 1; d is 32, 64, 96 or 128; 16-byte aligned pointers; other
+ *  - Nq, Nk >= 1; d is 32, 64, 96, 128 or 256; 16-byte aligned pointers; other
  *    conventions (scale, kv_lens, stream, errors) as for fa_fwd.  With
  *    contiguous strides, Nq = Nk and no window it computes exactly fa_fwd. */
 int fa_fwd_general(const void* q, const void* k, const void* v, void* o, float* lse,
