@@ -17,9 +17,9 @@
 //  * One workgroup = 8 wavefronts = one block of 256 query rows of one
 //    (batch, head); each wave owns 32 rows, the N dimension of a 32x32 MFMA
 //    tile.  Two waves share each SIMD, so one wave's MFMAs overlap the
-//    other's softmax.  Blocks of 64 keys are staged through LDS, double
-//    buffered: raw buffer loads bring block j+1 into registers while block j
-//    is computed (rows past the end read as zero).  LDS operand reads are
+//    other's softmax.  Blocks of 64 keys (128 for d <= 64) are staged
+//    through LDS, double buffered: raw buffer loads bring block j+1 into
+//    registers while block j is computed (rows past the end read as zero).  LDS operand reads are
 //    issued well ahead of their MFMAs (scheduling hints), since an LDS round
 //    trip under load spans about ten MFMA issue intervals.
 //  * Scores are computed transposed, S^T = K Q^T, with
@@ -238,7 +238,10 @@ void fa_fwd_bf16_kernel(Params p) {
   constexpr bool GEN = MODE != 0;
   constexpr bool VL = MODE == 2;
   constexpr int kThreads = 64 * NW;
-  constexpr int BN = 64;            // keys per block
+  // Keys per block: 128 for d <= 64, where the softmax work per MFMA is
+  // largest and halving the per-block loop, barrier and staging overhead
+  // pays; 64 otherwise (the register budget).
+  constexpr int BN = D <= 64 ? 128 : 64;
   constexpr int BM = 32 * NW;       // query rows per workgroup
   constexpr int KS = D / 16;        // MFMA k-steps over d for S^T
   constexpr int DT = D / 32;        // 32-row tiles of O^T
