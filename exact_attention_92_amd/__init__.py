@@ -2,7 +2,7 @@
 
 The binding only marshals arguments: every step of the forward and backward
 passes runs in the HIP kernels of ``csrc/fa_fwd.hip``, ``csrc/fa_fwd_fp8.hip``,
-``csrc/fa_bwd.hip`` and ``csrc/fa_decode.hip``.  PyTorch supplies device memory and
+``csrc/fa_bwd_kernels.h`` and ``csrc/fa_decode.hip``.  PyTorch supplies device memory and
 the stream.  There is no CPU or PyTorch fallback: if the library is missing
 or the GPU is absent, the calls raise.
 

@@ -11,7 +11,8 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", f) for f in ("fa_fwd.hip", "fa_bwd.hip", "fa_fwd_fp8.hip", "fa_decode.hip")]
+SRCS = [os.path.join(PKG, "csrc", f)
+        for f in ("fa_fwd.hip", "fa_bwd.hip", "fa_bwd_d64.hip", "fa_fwd_fp8.hip", "fa_decode.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa92.so")
 ARCH = "gfx950"
@@ -26,9 +27,12 @@ HIPCC_FLAGS = [
 # ordinary VGPRs: left to its own choice the compiler moves the d = 256
 # kernel's accumulators into AGPRs and copies them back on every block
 # (425 -> 732 TFLOP/s at d = 256; the d <= 128 kernels never need AGPRs and
-# are unchanged).  The backward's dK/dV kernel needs ~450 registers and is
-# left to the compiler's default.
-SRC_FLAGS = {"fa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# are unchanged).  The backward's d = 64 kernels too (8-15% faster: the dK/dV
+# kernel then needs no AGPR<->VGPR copies); its d = 128 kernels (fa_bwd.hip,
+# ~450 registers in dK/dV) are left to the compiler's default, which is 2%
+# faster there.
+SRC_FLAGS = {"fa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+             "fa_bwd_d64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc() -> str:
