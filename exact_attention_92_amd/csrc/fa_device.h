@@ -88,11 +88,12 @@ __device__ __forceinline__ void transpose4x8(const u32x4_t (&x)[4], u32x2_t (&ou
 
 // Workgroups are dispatched round-robin over the 8 XCDs (w % 8), in order
 // within one.  Maps the linear workgroup id to (head, block) so that when the
-// heads split evenly XCD x owns a contiguous range of heads (their tensors
-// share its L2) and visits their blocks rank by rank, FA_WORK_GROUP (four)
-// heads at a time;
-// rank 0 is block nb-1 when heavy_last, else block 0.  Otherwise XCD x gets
-// the contiguous logical range [x*G/8, (x+1)*G/8).
+// heads split evenly XCD x owns the heads bh = x, x + 8, x + 16, ... (each
+// head's tensors stay in one XCD's L2, and every XCD gets heads of every
+// batch entry, so per-batch key lengths balance across XCDs) and visits
+// their blocks rank by rank, FA_WORK_GROUP (four) heads at a time; rank 0 is
+// block nb-1 when heavy_last, else block 0.  Otherwise XCD x gets the
+// contiguous logical range [x*G/8, (x+1)*G/8).
 #ifndef FA_WORK_GROUP
 #define FA_WORK_GROUP 4
 #endif
@@ -104,7 +105,7 @@ __device__ __forceinline__ void map_work(int nb, bool heavy_last, int& bh, int& 
     const int hx = BH / 8, i = w / 8;
     const int g = (hx % FA_WORK_GROUP == 0) ? FA_WORK_GROUP : hx;
     const int grp = i / (g * nb), j = i - grp * (g * nb);
-    bh = (w % 8) * hx + grp * g + j % g;
+    bh = (grp * g + j % g) * 8 + (w % 8);
     const int r = j / g;
     blk = heavy_last ? (nb - 1 - r) : r;
     return;

@@ -151,11 +151,14 @@ __device__ __forceinline__ void mfma_read_ahead() {
 #endif
 // Maps the linear workgroup id to (head, query block).  Workgroups are
 // dispatched round-robin over the 8 XCDs (w % 8), and in order within one.
-// When the heads split evenly, XCD x owns a contiguous range of heads (their
-// K/V share its L2) and visits their query blocks rank by rank: for causal
-// masks the last (heaviest) query block of every head first, so the light
-// ones fill the tail.  Otherwise XCD x gets the contiguous logical range
-// [x*G/8, (x+1)*G/8), heavy query blocks first within each head.
+// When the heads split evenly, XCD x owns the heads bh = x, x + 8, x + 16, ...
+// (each head's K/V stays in one XCD's L2; striding rather than a contiguous
+// range gives every XCD heads of every batch entry, so per-batch key
+// lengths do not load one XCD more than another) and visits their query
+// blocks rank by rank: for causal masks the last (heaviest) query block of
+// every head first, so the light ones fill the tail.  Otherwise XCD x gets
+// the contiguous logical range [x*G/8, (x+1)*G/8), heavy query blocks first
+// within each head.
 //
 // With spread (packed sequences of unequal lengths, where binding heads to
 // XCDs would bind whole sequences to them), the order is rank-major over all
@@ -173,12 +176,12 @@ __device__ __forceinline__ void map_block(int nqb, bool causal, int& bh, int& qb
     return;
   }
   if (G % 8 == 0 && BH % 8 == 0) {
-    // XCD x = w % 8 owns heads [x*BH/8, (x+1)*BH/8); it visits their query
+    // XCD x = w % 8 owns heads x + 8t, t < BH/8; it visits their query
     // blocks rank by rank (heaviest causal rank first), head by head.
     const int hx = BH / 8, i = w / 8;
     const int g = (hx % FA_HEAD_GROUP == 0) ? FA_HEAD_GROUP : hx;   // heads visited together
     const int grp = i / (g * nqb), j = i - grp * (g * nqb);
-    bh = (w % 8) * hx + grp * g + j % g;
+    bh = (grp * g + j % g) * 8 + (w % 8);
     const int r = j / g;
     qb = causal ? (nqb - 1 - r) : r;
     return;
