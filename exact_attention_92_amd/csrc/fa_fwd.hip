@@ -51,10 +51,12 @@
 //    a wave skips the blocks above its own rows; only blocks that cross the
 //    diagonal, the key-padding edge or the sequence end are masked
 //    element-wise ("Causal Mask怎么处理" on the gentlecold.top page).
-//  * Workgroups are dispatched round-robin over the 8 XCDs; the block index
-//    is remapped so that consecutive work items of one head land on one XCD
-//    (shared L2 for that head's K/V), and causal query blocks run heaviest
-//    first.
+//  * Workgroups are dispatched round-robin over the 8 XCDs; the work items
+//    (head, query block) are ordered so that all items of one head land on
+//    one XCD (shared L2 for that head's K/V) and causal query blocks run
+//    heaviest first.  For contiguous self-attention the grid is capped at
+//    the workgroups the chip holds at once and each workgroup loops over its
+//    items in a snake order.
 //  * One kernel template serves three entry points: contiguous
 //    self-attention (fa_fwd), the general layout with N_q != N_k, a sliding
 //    window and arbitrary strides (fa_fwd_general), and packed sequences of
@@ -62,6 +64,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <algorithm>
 
 #include "fa_api.h"
 
@@ -165,9 +169,7 @@ __device__ __forceinline__ void mfma_read_ahead() {
 // (batch, head): consecutive workgroups, and so the XCDs, take every
 // sequence's blocks of one rank before the next rank.
 __device__ __forceinline__ void map_block(int nqb, bool causal, int& bh, int& qb,
-                                          bool spread = false) {
-  const int G = gridDim.x;
-  const int w = blockIdx.x;
+                                          bool spread, int w, int G) {
   const int BH = G / nqb;
   if (spread) {
     bh = w % BH;
@@ -200,6 +202,7 @@ struct Params {
   float* lse;
   const int32_t* kv_lens;
   int H, N, nqb;    // N: query rows (and keys, unless the general layout is used)
+  int items;        // work items (head, query block) = B * H * nqb
   float c;          // |scale| * log2(e), >= kMinScale * log2(e)
   unsigned qsign;   // sign flip applied to Q when scale < 0
   int causal;
@@ -270,279 +273,292 @@ void fa_fwd_bf16_kernel(Params p) {
   const int n = lane & 31;
   const int hf = lane >> 5;
   const bool causal = p.causal != 0;
-  int N = p.N;
+  // Work items: this workgroup takes items in rounds, snaking (odd rounds
+  // visit the positions in reverse) so heavy and light causal blocks even out;
+  // with 8 | G and 8 | P the items of a round keep their XCD lane.
+  const int P = gridDim.x, G = p.items;
+  const bool lanes8 = !VL && G % 8 == 0 && P % 8 == 0;
+  const int L8 = lanes8 ? 8 : 1;
+  const int lx = blockIdx.x % L8, mx = blockIdx.x / L8, Pm = P / L8, Gm = G / L8;
+  for (int round = 0;; ++round) {
+    const int idx = round * Pm + ((round & 1) ? Pm - 1 - mx : mx);
+    if (idx >= Gm) break;
+    const int w_item = idx * L8 + lx;
+    if (round > 0) __syncthreads();
+    int N = p.N;
 
-  int bh, qb;
-  map_block(p.nqb, causal, bh, qb, VL);
-  const int b = bh / p.H;
-  int Nk = GEN ? p.Nk : N;
-  int off = GEN ? p.off : 0;                // key position of query row 0
-  long long qr0 = 0, kr0 = 0;               // varlen: first packed row of the sequence
-  if (VL) {
-    // Boundaries clamped into the packed tensors, so any cu values stay in bounds.
-    const long long q_s = min(max((long long)p.cu_q[b], 0LL), p.total_q);
-    const long long q_e = min(max((long long)p.cu_q[b + 1], q_s), p.total_q);
-    const long long k_s = min(max((long long)p.cu_k[b], 0LL), p.total_k);
-    const long long k_e = min(max((long long)p.cu_k[b + 1], k_s), p.total_k);
-    N = (int)(q_e - q_s);
-    Nk = (int)(k_e - k_s);
-    off = Nk - N;
-    qr0 = q_s;
-    kr0 = k_s;
-    if (qb * (32 * NW) >= N) return;        // whole workgroup past the sequence's rows
-  }
-  const int W = GEN ? p.window : -1;        // keys visible before a query's own position
-  const uint32_t QRB = GEN ? p.qrs : ROWB;  // row strides in bytes
-  const uint32_t KRB = GEN ? p.krs : ROWB;
-  const uint32_t VRB = GEN ? p.vrs : ROWB;
-  const size_t hoff = (size_t)bh * (size_t)N * D;
-  const int hh = bh - b * p.H;
-  const uint16_t* Qh = (const uint16_t*)p.q +
-                       (GEN ? b * p.qbs + hh * p.qhs + qr0 * (QRB / 2) : (long long)hoff);
-  const uint16_t* Kh = (const uint16_t*)p.k +
-                       (GEN ? b * p.kbs + hh * p.khs + kr0 * (KRB / 2) : (long long)hoff);
-  const uint16_t* Vh = (const uint16_t*)p.v +
-                       (GEN ? b * p.vbs + hh * p.vhs + kr0 * (VRB / 2) : (long long)hoff);
-
-  int n_vis = Nk;
-  if (p.kv_lens) {
-    const int kl = p.kv_lens[b];
-    n_vis = kl < 0 ? 0 : (kl > Nk ? Nk : kl);
-  }
-  const int q0 = qb * BM;
-  const int qw0 = q0 + wave * 32;
-  const int kend = causal ? min(n_vis, q0 + BM + off) : n_vis;
-  const int nblk = (kend + BN - 1) / BN;
-  // With a window, blocks entirely before the first row's window are skipped.
-  const int jstart = (W >= 0) ? max(0, q0 + off - W) / BN : 0;
-
-  // Q rows of this wave in the B-operand layout of S^T = K Q^T.  Rows past N
-  // lie outside the buffer range and read as zero.
-  u32x4_t qr[KS];
-  {
-    const rsrc_t rq = make_rsrc(Qh, (uint32_t)N * QRB);
-    const uint32_t qoff = (uint32_t)(qw0 + n) * QRB + 16u * hf;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qr[ks] = buf_load16(rq, qoff + 32u * ks) ^ p.qsign;
-  }
-
-  // Global -> register staging of key block j.  K: row-major 16-byte
-  // pieces.  V: pieces of 4 keys x 8 dims, written to LDS transposed.  The
-  // buffer range of V ends at the last visible key, so hidden V rows arrive
-  // as zeros; K rows past N read zero.
-  uint32_t k_off[KU];
-#pragma unroll
-  for (int u = 0; u < KU; ++u) {
-    const int unit = tid + u * kThreads;
-    // A thread without a piece reads past every buffer range (zeros).
-    k_off[u] = (KFULL || unit < KUNITS) ? (uint32_t)(unit / CPR) * KRB + 16u * (unit % CPR)
-                                        : 0x80000000u;
-  }
-  bool v_unit[VU];
-  int vkg[VU], vdc[VU];
-  uint32_t v_off[VU];
-#pragma unroll
-  for (int u = 0; u < VU; ++u) {
-    const int unit = tid + u * kThreads;
-    v_unit[u] = unit < VUNITS;
-    vkg[u] = unit % (BN / 4);
-    vdc[u] = unit / (BN / 4);
-    v_off[u] = (uint32_t)(4 * vkg[u]) * VRB + 16u * vdc[u];
-  }
-  u32x4_t kreg[KU], vreg[VU][4];
-  auto load_block = [&](int j) {
-    const int kbase = j * BN;
-    const rsrc_t rk = make_rsrc(Kh + (size_t)kbase * (KRB / 2), (uint32_t)max(0, Nk - kbase) * KRB);
-    const rsrc_t rv = make_rsrc(Vh + (size_t)kbase * (VRB / 2), (uint32_t)max(0, n_vis - kbase) * VRB);
-#pragma unroll
-    for (int u = 0; u < KU; ++u) kreg[u] = buf_load16(rk, k_off[u]);
-#pragma unroll
-    for (int u = 0; u < VU; ++u) {
-      if (v_unit[u]) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vreg[u][i] = buf_load16(rv, v_off[u] + i * VRB);
-      }
+    int bh, qb;
+    map_block(p.nqb, causal, bh, qb, VL, w_item, p.items);
+    const int b = bh / p.H;
+    int Nk = GEN ? p.Nk : N;
+    int off = GEN ? p.off : 0;                // key position of query row 0
+    long long qr0 = 0, kr0 = 0;               // varlen: first packed row of the sequence
+    if (VL) {
+      // Boundaries clamped into the packed tensors, so any cu values stay in bounds.
+      const long long q_s = min(max((long long)p.cu_q[b], 0LL), p.total_q);
+      const long long q_e = min(max((long long)p.cu_q[b + 1], q_s), p.total_q);
+      const long long k_s = min(max((long long)p.cu_k[b], 0LL), p.total_k);
+      const long long k_e = min(max((long long)p.cu_k[b + 1], k_s), p.total_k);
+      N = (int)(q_e - q_s);
+      Nk = (int)(k_e - k_s);
+      off = Nk - N;
+      qr0 = q_s;
+      kr0 = k_s;
+      if (qb * (32 * NW) >= N) continue;      // whole workgroup past the sequence's rows
     }
-  };
-  auto store_block = [&](int buf) {
-#pragma unroll
+    const int W = GEN ? p.window : -1;        // keys visible before a query's own position
+    const uint32_t QRB = GEN ? p.qrs : ROWB;  // row strides in bytes
+    const uint32_t KRB = GEN ? p.krs : ROWB;
+    const uint32_t VRB = GEN ? p.vrs : ROWB;
+    const size_t hoff = (size_t)bh * (size_t)N * D;
+    const int hh = bh - b * p.H;
+    const uint16_t* Qh = (const uint16_t*)p.q +
+                         (GEN ? b * p.qbs + hh * p.qhs + qr0 * (QRB / 2) : (long long)hoff);
+    const uint16_t* Kh = (const uint16_t*)p.k +
+                         (GEN ? b * p.kbs + hh * p.khs + kr0 * (KRB / 2) : (long long)hoff);
+    const uint16_t* Vh = (const uint16_t*)p.v +
+                         (GEN ? b * p.vbs + hh * p.vhs + kr0 * (VRB / 2) : (long long)hoff);
+
+    int n_vis = Nk;
+    if (p.kv_lens) {
+      const int kl = p.kv_lens[b];
+      n_vis = kl < 0 ? 0 : (kl > Nk ? Nk : kl);
+    }
+    const int q0 = qb * BM;
+    const int qw0 = q0 + wave * 32;
+    const int kend = causal ? min(n_vis, q0 + BM + off) : n_vis;
+    const int nblk = (kend + BN - 1) / BN;
+    // With a window, blocks entirely before the first row's window are skipped.
+    const int jstart = (W >= 0) ? max(0, q0 + off - W) / BN : 0;
+
+    // Q rows of this wave in the B-operand layout of S^T = K Q^T.  Rows past N
+    // lie outside the buffer range and read as zero.
+    u32x4_t qr[KS];
+    {
+      const rsrc_t rq = make_rsrc(Qh, (uint32_t)N * QRB);
+      const uint32_t qoff = (uint32_t)(qw0 + n) * QRB + 16u * hf;
+  #pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qr[ks] = buf_load16(rq, qoff + 32u * ks) ^ p.qsign;
+    }
+
+    // Global -> register staging of key block j.  K: row-major 16-byte
+    // pieces.  V: pieces of 4 keys x 8 dims, written to LDS transposed.  The
+    // buffer range of V ends at the last visible key, so hidden V rows arrive
+    // as zeros; K rows past N read zero.
+    uint32_t k_off[KU];
+  #pragma unroll
     for (int u = 0; u < KU; ++u) {
       const int unit = tid + u * kThreads;
-      if (KFULL || unit < KUNITS) *(u32x4_t*)&k_lds[buf][unit / CPR][8 * (unit % CPR)] = kreg[u];
+      // A thread without a piece reads past every buffer range (zeros).
+      k_off[u] = (KFULL || unit < KUNITS) ? (uint32_t)(unit / CPR) * KRB + 16u * (unit % CPR)
+                                          : 0x80000000u;
     }
-#pragma unroll
+    bool v_unit[VU];
+    int vkg[VU], vdc[VU];
+    uint32_t v_off[VU];
+  #pragma unroll
     for (int u = 0; u < VU; ++u) {
-      if (v_unit[u]) {
-        // Dword w of key i holds dims 8*vdc + 2w, +1: regroup into
-        // (keys 0-3 of dim 2w) and (keys 0-3 of dim 2w+1).
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const unsigned a0 = vreg[u][0][w], a1 = vreg[u][1][w], a2 = vreg[u][2][w],
-                         a3 = vreg[u][3][w];
-          const u32x2_t lo = {__builtin_amdgcn_perm(a1, a0, 0x05040100u),
-                              __builtin_amdgcn_perm(a3, a2, 0x05040100u)};
-          const u32x2_t hi = {__builtin_amdgcn_perm(a1, a0, 0x07060302u),
-                              __builtin_amdgcn_perm(a3, a2, 0x07060302u)};
-          *(u32x2_t*)&vt_lds[buf][8 * vdc[u] + 2 * w][4 * vkg[u]] = lo;
-          *(u32x2_t*)&vt_lds[buf][8 * vdc[u] + 2 * w + 1][4 * vkg[u]] = hi;
+      const int unit = tid + u * kThreads;
+      v_unit[u] = unit < VUNITS;
+      vkg[u] = unit % (BN / 4);
+      vdc[u] = unit / (BN / 4);
+      v_off[u] = (uint32_t)(4 * vkg[u]) * VRB + 16u * vdc[u];
+    }
+    u32x4_t kreg[KU], vreg[VU][4];
+    auto load_block = [&](int j) {
+      const int kbase = j * BN;
+      const rsrc_t rk = make_rsrc(Kh + (size_t)kbase * (KRB / 2), (uint32_t)max(0, Nk - kbase) * KRB);
+      const rsrc_t rv = make_rsrc(Vh + (size_t)kbase * (VRB / 2), (uint32_t)max(0, n_vis - kbase) * VRB);
+  #pragma unroll
+      for (int u = 0; u < KU; ++u) kreg[u] = buf_load16(rk, k_off[u]);
+  #pragma unroll
+      for (int u = 0; u < VU; ++u) {
+        if (v_unit[u]) {
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) vreg[u][i] = buf_load16(rv, v_off[u] + i * VRB);
         }
       }
-    }
-  };
-
-  float m_run = -INFINITY;   // reference max, log2 units (one query row per lane)
-  float l_run = 0.f;         // row sum of the bf16-rounded probabilities (normalises O)
-  float le_run = 0.f;        // row sum of the fp32 probabilities (gives LSE)
-  f32x16_t acc[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
-  const float c = p.c;
-  const int krow = k_row_perm(n);
-  bool have_ref = false;   // wave-uniform: m_run was set by a full pass
-
-  // p = 2^(s*c - base), packed to bf16 as P^T (chunk pc = registers
-  // 8(pc%2)..+7 of key tile pc/2 = keys 16pc + 8hf + 0..7) with both row
-  // sums; the scores are left intact.
-  auto exps = [&](const f32x16_t (&s)[KT], u32x4_t (&pb)[PC], float base, float& re,
-                  float& rs) {
-    float re0 = 0.f, re1 = 0.f, rs0 = 0.f, rs1 = 0.f;
-#pragma unroll
-    for (int pc = 0; pc < PC; ++pc) {
-      const int kt = pc >> 1, r0 = 8 * (pc & 1);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r0 + 2 * w], c, -base));
-        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r0 + 2 * w + 1], c, -base));
-        re0 += e0;
-        re1 += e1;
-        pb[pc][w] = pack_bf16(e0, e1);
+    };
+    auto store_block = [&](int buf) {
+  #pragma unroll
+      for (int u = 0; u < KU; ++u) {
+        const int unit = tid + u * kThreads;
+        if (KFULL || unit < KUNITS) *(u32x4_t*)&k_lds[buf][unit / CPR][8 * (unit % CPR)] = kreg[u];
       }
-      rs0 = sum_bf16x2(pb[pc][0], sum_bf16x2(pb[pc][1], rs0));
-      rs1 = sum_bf16x2(pb[pc][2], sum_bf16x2(pb[pc][3], rs1));
-    }
-    re = re0 + re1;
-    rs = rs0 + rs1;
-  };
-
-  if (jstart < nblk) {
-    load_block(jstart);
-    store_block(0);
-  }
-  __syncthreads();
-
-  for (int j = jstart; j < nblk; ++j) {
-    const int buf = (j - jstart) & 1;
-    const bool more = j + 1 < nblk;
-    if (more) load_block(j + 1);
-    const int kbase = j * BN;
-    const bool wave_skip = (causal && (kbase > qw0 + 31 + off)) ||
-                           (W >= 0 && kbase + BN - 1 < qw0 + off - W);
-    if (!wave_skip) {
-      // S^T = K_j Q^T with K rows permuted (row 32kt + krow feeds MFMA row n).
-      f32x16_t s[KT];
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-          const u32x4_t a = *(const u32x4_t*)&k_lds[buf][32 * kt + krow][16 * ks + 8 * hf];
-          s[kt] = mfma_bf16(a, qr[ks], s[kt]);
-        }
-      mfma_read_ahead<KS * KT, FA_READ_AHEAD>();
-      // The first V^T operands are requested now, so they arrive while the
-      // softmax runs.
-      constexpr int VPRE = FA_V_PREFETCH < PC * DT ? FA_V_PREFETCH : PC * DT;
-      u32x4_t vpre[VPRE > 0 ? VPRE : 1];
-#pragma unroll
-      for (int i = 0; i < VPRE; ++i)
-        vpre[i] = *(const u32x4_t*)&vt_lds[buf][32 * (i % DT) + n][16 * (i / DT) + 8 * hf];
-      // Register r of key tile kt holds key kbase + 32kt + 16(r/8) + 8hf + r%8.
-      if ((causal && kbase + BN - 1 > qw0 + off) || kbase + BN > n_vis ||
-          (W >= 0 && kbase < qw0 + 31 + off - W)) {
-        const int qrow = qw0 + n;
-        const int lim = (causal ? min(qrow + off, n_vis - 1) : n_vis - 1) - kbase - 8 * hf;
-        const int lim_lo = (W >= 0) ? qrow + off - W - kbase - 8 * hf : -BN;
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int idx = 32 * kt + 16 * (r >> 3) + (r & 7);
-            if (idx > lim || idx < lim_lo) s[kt][r] = -INFINITY;
+  #pragma unroll
+      for (int u = 0; u < VU; ++u) {
+        if (v_unit[u]) {
+          // Dword w of key i holds dims 8*vdc + 2w, +1: regroup into
+          // (keys 0-3 of dim 2w) and (keys 0-3 of dim 2w+1).
+  #pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const unsigned a0 = vreg[u][0][w], a1 = vreg[u][1][w], a2 = vreg[u][2][w],
+                           a3 = vreg[u][3][w];
+            const u32x2_t lo = {__builtin_amdgcn_perm(a1, a0, 0x05040100u),
+                                __builtin_amdgcn_perm(a3, a2, 0x05040100u)};
+            const u32x2_t hi = {__builtin_amdgcn_perm(a1, a0, 0x07060302u),
+                                __builtin_amdgcn_perm(a3, a2, 0x07060302u)};
+            *(u32x2_t*)&vt_lds[buf][8 * vdc[u] + 2 * w][4 * vkg[u]] = lo;
+            *(u32x2_t*)&vt_lds[buf][8 * vdc[u] + 2 * w + 1][4 * vkg[u]] = hi;
           }
-      }
-
-      // Exponentials against the reference max.  A wave's first block, or a
-      // block whose fp32 row sum shows a probability above 2^20 (or an
-      // infinite one), takes the full path: block row max, move the
-      // reference, rescale the state, redo the exponentials.
-      u32x4_t pb[PC];
-      float re = 0.f, rs = 0.f;
-      bool full = !have_ref;
-      if (!full) {
-        exps(s, pb, m_run, re, rs);
-        full = __any(!(re <= kOverflowSum));
-      }
-      if (full) {
-        float mx = s[0][0];
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-        const float m_new = fmaxf(m_run, pair_max(mx) * c);
-        const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
-        l_run *= alpha;
-        le_run *= alpha;
-        m_run = m_new;
-        have_ref = true;
-        exps(s, pb, (m_new == -INFINITY) ? 0.f : m_new, re, rs);
-      }
-      l_run += rs;
-      le_run += re;
-
-      // O^T += V_j^T P^T: A operand = V^T rows 32dt + n, keys 16pc + 8hf + 0..7.
-#pragma unroll
-      for (int pc = 0; pc < PC; ++pc)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const int i = pc * DT + dt;
-          const u32x4_t a = i < VPRE ? vpre[i < VPRE ? i : 0]
-                                     : *(const u32x4_t*)&vt_lds[buf][32 * dt + n][16 * pc + 8 * hf];
-          acc[dt] = mfma_bf16(a, pb[pc], acc[dt]);
         }
-      mfma_read_ahead<PC * DT, (PC * DT - VPRE < FA_READ_AHEAD ? PC * DT - VPRE : FA_READ_AHEAD)>();
-    }
-    if (more) store_block(buf ^ 1);
-    __syncthreads();
-  }
-
-  // Epilogue: O = acc / l (rounded to bf16 once), LSE = (m + log2 le) * ln 2.
-  uint16_t* __restrict__ Oh =
-      (uint16_t*)p.o + (GEN ? b * p.obs + hh * p.ohs + qr0 * p.ors : (long long)hoff);
-  float* __restrict__ Lh = p.lse + (VL ? hh * p.total_q + qr0 : (long long)bh * N);
-  const float lt = pair_sum(l_run);
-  const float le = pair_sum(le_run);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  const int qrow = qw0 + n;
-  if (qrow < N) {
-    uint16_t* orow = Oh + (size_t)qrow * (GEN ? (size_t)p.ors : (size_t)D);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        u32x2_t x = {pack_bf16(acc[dt][4 * a] * inv, acc[dt][4 * a + 1] * inv),
-                     pack_bf16(acc[dt][4 * a + 2] * inv, acc[dt][4 * a + 3] * inv)};
-        *(u32x2_t*)(orow + 32 * dt + 8 * a + 4 * hf) = x;
       }
-    if (hf == 0) Lh[qrow] = lt > 0.f ? (m_run + __builtin_amdgcn_logf(le)) * kLn2 : -INFINITY;
+    };
+
+    float m_run = -INFINITY;   // reference max, log2 units (one query row per lane)
+    float l_run = 0.f;         // row sum of the bf16-rounded probabilities (normalises O)
+    float le_run = 0.f;        // row sum of the fp32 probabilities (gives LSE)
+    f32x16_t acc[DT];
+  #pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+  #pragma unroll
+      for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
+    const float c = p.c;
+    const int krow = k_row_perm(n);
+    bool have_ref = false;   // wave-uniform: m_run was set by a full pass
+
+    // p = 2^(s*c - base), packed to bf16 as P^T (chunk pc = registers
+    // 8(pc%2)..+7 of key tile pc/2 = keys 16pc + 8hf + 0..7) with both row
+    // sums; the scores are left intact.
+    auto exps = [&](const f32x16_t (&s)[KT], u32x4_t (&pb)[PC], float base, float& re,
+                    float& rs) {
+      float re0 = 0.f, re1 = 0.f, rs0 = 0.f, rs1 = 0.f;
+  #pragma unroll
+      for (int pc = 0; pc < PC; ++pc) {
+        const int kt = pc >> 1, r0 = 8 * (pc & 1);
+  #pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r0 + 2 * w], c, -base));
+          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r0 + 2 * w + 1], c, -base));
+          re0 += e0;
+          re1 += e1;
+          pb[pc][w] = pack_bf16(e0, e1);
+        }
+        rs0 = sum_bf16x2(pb[pc][0], sum_bf16x2(pb[pc][1], rs0));
+        rs1 = sum_bf16x2(pb[pc][2], sum_bf16x2(pb[pc][3], rs1));
+      }
+      re = re0 + re1;
+      rs = rs0 + rs1;
+    };
+
+    if (jstart < nblk) {
+      load_block(jstart);
+      store_block(0);
+    }
+    __syncthreads();
+
+    for (int j = jstart; j < nblk; ++j) {
+      const int buf = (j - jstart) & 1;
+      const bool more = j + 1 < nblk;
+      if (more) load_block(j + 1);
+      const int kbase = j * BN;
+      const bool wave_skip = (causal && (kbase > qw0 + 31 + off)) ||
+                             (W >= 0 && kbase + BN - 1 < qw0 + off - W);
+      if (!wave_skip) {
+        // S^T = K_j Q^T with K rows permuted (row 32kt + krow feeds MFMA row n).
+        f32x16_t s[KT];
+  #pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+  #pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+  #pragma unroll
+          for (int kt = 0; kt < KT; ++kt) {
+            const u32x4_t a = *(const u32x4_t*)&k_lds[buf][32 * kt + krow][16 * ks + 8 * hf];
+            s[kt] = mfma_bf16(a, qr[ks], s[kt]);
+          }
+        mfma_read_ahead<KS * KT, FA_READ_AHEAD>();
+        // The first V^T operands are requested now, so they arrive while the
+        // softmax runs.
+        constexpr int VPRE = FA_V_PREFETCH < PC * DT ? FA_V_PREFETCH : PC * DT;
+        u32x4_t vpre[VPRE > 0 ? VPRE : 1];
+  #pragma unroll
+        for (int i = 0; i < VPRE; ++i)
+          vpre[i] = *(const u32x4_t*)&vt_lds[buf][32 * (i % DT) + n][16 * (i / DT) + 8 * hf];
+        // Register r of key tile kt holds key kbase + 32kt + 16(r/8) + 8hf + r%8.
+        if ((causal && kbase + BN - 1 > qw0 + off) || kbase + BN > n_vis ||
+            (W >= 0 && kbase < qw0 + 31 + off - W)) {
+          const int qrow = qw0 + n;
+          const int lim = (causal ? min(qrow + off, n_vis - 1) : n_vis - 1) - kbase - 8 * hf;
+          const int lim_lo = (W >= 0) ? qrow + off - W - kbase - 8 * hf : -BN;
+  #pragma unroll
+          for (int kt = 0; kt < KT; ++kt)
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int idx = 32 * kt + 16 * (r >> 3) + (r & 7);
+              if (idx > lim || idx < lim_lo) s[kt][r] = -INFINITY;
+            }
+        }
+
+        // Exponentials against the reference max.  A wave's first block, or a
+        // block whose fp32 row sum shows a probability above 2^20 (or an
+        // infinite one), takes the full path: block row max, move the
+        // reference, rescale the state, redo the exponentials.
+        u32x4_t pb[PC];
+        float re = 0.f, rs = 0.f;
+        bool full = !have_ref;
+        if (!full) {
+          exps(s, pb, m_run, re, rs);
+          full = __any(!(re <= kOverflowSum));
+        }
+        if (full) {
+          float mx = s[0][0];
+  #pragma unroll
+          for (int kt = 0; kt < KT; ++kt)
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
+          const float m_new = fmaxf(m_run, pair_max(mx) * c);
+          const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+  #pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+          l_run *= alpha;
+          le_run *= alpha;
+          m_run = m_new;
+          have_ref = true;
+          exps(s, pb, (m_new == -INFINITY) ? 0.f : m_new, re, rs);
+        }
+        l_run += rs;
+        le_run += re;
+
+        // O^T += V_j^T P^T: A operand = V^T rows 32dt + n, keys 16pc + 8hf + 0..7.
+  #pragma unroll
+        for (int pc = 0; pc < PC; ++pc)
+  #pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const int i = pc * DT + dt;
+            const u32x4_t a = i < VPRE ? vpre[i < VPRE ? i : 0]
+                                       : *(const u32x4_t*)&vt_lds[buf][32 * dt + n][16 * pc + 8 * hf];
+            acc[dt] = mfma_bf16(a, pb[pc], acc[dt]);
+          }
+        mfma_read_ahead<PC * DT, (PC * DT - VPRE < FA_READ_AHEAD ? PC * DT - VPRE : FA_READ_AHEAD)>();
+      }
+      if (more) store_block(buf ^ 1);
+      __syncthreads();
+    }
+
+    // Epilogue: O = acc / l (rounded to bf16 once), LSE = (m + log2 le) * ln 2.
+    uint16_t* __restrict__ Oh =
+        (uint16_t*)p.o + (GEN ? b * p.obs + hh * p.ohs + qr0 * p.ors : (long long)hoff);
+    float* __restrict__ Lh = p.lse + (VL ? hh * p.total_q + qr0 : (long long)bh * N);
+    const float lt = pair_sum(l_run);
+    const float le = pair_sum(le_run);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const int qrow = qw0 + n;
+    if (qrow < N) {
+      uint16_t* orow = Oh + (size_t)qrow * (GEN ? (size_t)p.ors : (size_t)D);
+  #pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+  #pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          u32x2_t x = {pack_bf16(acc[dt][4 * a] * inv, acc[dt][4 * a + 1] * inv),
+                       pack_bf16(acc[dt][4 * a + 2] * inv, acc[dt][4 * a + 3] * inv)};
+          *(u32x2_t*)(orow + 32 * dt + 8 * a + 4 * hf) = x;
+        }
+      if (hf == 0) Lh[qrow] = lt > 0.f ? (m_run + __builtin_amdgcn_logf(le)) * kLn2 : -INFINITY;
+    }
   }
 }
 
@@ -572,7 +588,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(Params p) {
   const int N = p.N;
 
   int bh, qb;
-  map_block(p.nqb, causal, bh, qb);
+  map_block(p.nqb, causal, bh, qb, false, blockIdx.x, gridDim.x);
   const int b = bh / p.H;
   const size_t hoff = (size_t)bh * (size_t)N * D;
   const float* __restrict__ Qh = (const float*)p.q + hoff;
@@ -737,19 +753,52 @@ Params make_params(const void* q, const void* k, const void* v, void* o, float* 
 constexpr long long kCUs = 256;   // compute units of an MI355X
 
 // One bf16 forward launch: 8-wave (256-row) workgroups when big, else 4-wave.
+// Workgroups of one kernel instantiation that the chip holds at once
+// (occupancy per compute unit x compute units), queried once.
+template <int D, int NW, int MODE>
+long long resident_workgroups() {
+  static const long long n = [] {
+    int occ = 0, dev = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fa_fwd_bf16_kernel<D, NW, MODE>,
+                                                     64 * NW, 0) != hipSuccess || occ < 1)
+      occ = 1;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+      cus = (int)kCUs;
+    (void)hipGetLastError();   // a failed query only changes the grid size
+    return (long long)occ * cus;
+  }();
+  return n;
+}
+
+// One launch over p.items work items.  Contiguous self-attention with
+// d <= 128 launches at most as many workgroups as the chip holds at once and
+// lets each loop over its items (no workgroup start per item; the snake order
+// of the kernel balances the causal ranks); the other layouts and d = 256
+// launch one workgroup per item.
+template <int D, int NW, int MODE>
+void launch_one(hipStream_t s, const Params& p) {
+  const long long grid = (MODE == 0 && D <= 128)
+                             ? std::min<long long>(p.items, resident_workgroups<D, NW, MODE>())
+                             : p.items;
+  hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, NW, MODE>), dim3((unsigned)grid), dim3(64 * NW), 0,
+                     s, p);
+}
+
+// 8-wave (256-row) workgroups when big, else 4-wave.
 template <int MODE>
-void launch_bf16(int d, bool big, dim3 grid, hipStream_t s, const Params& p) {
-  const dim3 block(big ? 512 : 256);
-#define FA_LAUNCH(DD)                                                                   \
-  if (big) hipLaunchKernelGGL((fa_fwd_bf16_kernel<DD, 8, MODE>), grid, block, 0, s, p); \
-  else hipLaunchKernelGGL((fa_fwd_bf16_kernel<DD, 4, MODE>), grid, block, 0, s, p)
+void launch_bf16(int d, bool big, hipStream_t s, const Params& p) {
+#define FA_LAUNCH(DD)                      \
+  if (big) launch_one<DD, 8, MODE>(s, p);  \
+  else launch_one<DD, 4, MODE>(s, p)
   switch (d) {
     case 32: FA_LAUNCH(32); break;
     case 64: FA_LAUNCH(64); break;
     case 96: FA_LAUNCH(96); break;
     case 128: FA_LAUNCH(128); break;
     default:   // 256: 4-wave (128-row) workgroups only, one wave per SIMD
-      hipLaunchKernelGGL((fa_fwd_bf16_kernel<256, 4, MODE>), grid, block, 0, s, p);
+      launch_one<256, 4, MODE>(s, p);
       break;
   }
 #undef FA_LAUNCH
@@ -771,8 +820,9 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
   const bool big = d != 256 && grid256 >= ((mask_kind & FA_MASK_CAUSAL) ? 2 : 1) * kCUs;
   const int BM = big ? 256 : 128;
   const int nqb = (N + BM - 1) / BM;
-  const Params p = make_params(q, k, v, o, lse, H, N, nqb, scale, mask_kind, kv_lens);
-  launch_bf16<0>(d, big, dim3((unsigned)(B * H * nqb)), s, p);
+  Params p = make_params(q, k, v, o, lse, H, N, nqb, scale, mask_kind, kv_lens);
+  p.items = B * H * nqb;
+  launch_bf16<0>(d, big, s, p);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -822,7 +872,8 @@ extern "C" int fa_fwd_general(const void* q, const void* k, const void* v, void*
   p.kbs = st[1][0]; p.khs = st[1][1]; p.krs = (unsigned)(st[1][2] * 2);
   p.vbs = st[2][0]; p.vhs = st[2][1]; p.vrs = (unsigned)(st[2][2] * 2);
   p.obs = st[3][0]; p.ohs = st[3][1]; p.ors = (unsigned)st[3][2];
-  launch_bf16<1>(d, big, dim3((unsigned)(B * H * nqb)), (hipStream_t)stream, p);
+  p.items = B * H * nqb;
+  launch_bf16<1>(d, big, (hipStream_t)stream, p);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -862,7 +913,8 @@ extern "C" int fa_fwd_varlen(const void* q, const void* k, const void* v, void* 
   p.cu_k = cu_seqlens_k;
   p.total_q = total_q;
   p.total_k = total_k;
-  launch_bf16<2>(d, big, dim3((unsigned)(B * H * nqb)), (hipStream_t)stream, p);
+  p.items = B * H * nqb;
+  launch_bf16<2>(d, big, (hipStream_t)stream, p);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
