@@ -17,6 +17,7 @@ from oracle import attention_general_ref, attention_varlen_ref
 
 pytestmark = pytest.mark.gpu
 
+
 DIMS = [32, 64, 96, 128, 256]
 EDGES = [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 191, 255, 256, 257, 383, 511, 513]
 
@@ -126,3 +127,25 @@ def test_random_packed_sequences(chunk):
         L = lse.cpu().numpy().astype(np.float64)      # [H, tq]
         compare_bound(O.transpose(1, 0, 2), L, (Or.transpose(1, 0, 2), Lr, M.transpose(1, 0, 2)),
                       what)
+
+
+@pytest.mark.parametrize("B,H,N,d,mask", [
+    (3, 37, 1000, 64, MASK_KEY_PADDING | 1),   # 888 work items > resident: looping, fallback order
+    (5, 29, 700, 32, MASK_KEY_PADDING),        # B*H not a multiple of 8
+    (2, 48, 1536, 128, 1),                     # 8-wave blocks, 8 | B*H, several rounds
+    (4, 30, 777, 96, 0),
+])
+def test_grids_larger_than_the_chip(B, H, N, d, mask):
+    """Grids with more work items than resident workgroups (each workgroup
+    loops over several items), with head counts that do and do not divide
+    by the XCD count, ragged N and mixed key lengths, on every element."""
+    kv_range = (1, N) if mask & MASK_KEY_PADDING else None
+    x = make_raw(B, H, N, d, "bf16", seed=B * 1000 + H + N + d, q_mult=2.0,
+                 kv_len_range=kv_range)
+    scale = d ** -0.5
+    what = f"fa_fwd B={B} H={H} N={N} d={d} mask={mask}"
+    say(what)
+    O, L = _run(x, scale, mask, -1, "bhnd", True)
+    ref = attention_general_ref(to_f64(x["q"]), to_f64(x["k"]), to_f64(x["v"]), scale, mask, -1,
+                                x.get("kv_lens"), magnitudes=True)
+    compare_bound(O, L, ref, what)
