@@ -19,9 +19,10 @@
 //    tile.  Two waves share each SIMD, so one wave's MFMAs overlap the
 //    other's softmax.  Blocks of 64 keys (128 for d <= 64) are staged
 //    through LDS, double buffered: raw buffer loads bring block j+1 into
-//    registers while block j is computed (rows past the end read as zero).  LDS operand reads are
-//    issued well ahead of their MFMAs (scheduling hints), since an LDS round
-//    trip under load spans about ten MFMA issue intervals.
+//    registers while block j is computed (rows past the end read as zero).
+//    LDS operand reads are issued well ahead of their MFMAs (scheduling
+//    hints), since an LDS round trip under load spans about ten MFMA issue
+//    intervals.
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: the accumulator holds ONE query row per lane
 //    (lane % 32) and 16 keys per lane, so the softmax row statistics are
@@ -337,7 +338,7 @@ void fa_fwd_bf16_kernel(Params p) {
     {
       const rsrc_t rq = make_rsrc(Qh, (uint32_t)N * QRB);
       const uint32_t qoff = (uint32_t)(qw0 + n) * QRB + 16u * hf;
-  #pragma unroll
+#pragma unroll
       for (int ks = 0; ks < KS; ++ks) qr[ks] = buf_load16(rq, qoff + 32u * ks) ^ p.qsign;
     }
 
@@ -346,7 +347,7 @@ void fa_fwd_bf16_kernel(Params p) {
     // buffer range of V ends at the last visible key, so hidden V rows arrive
     // as zeros; K rows past N read zero.
     uint32_t k_off[KU];
-  #pragma unroll
+#pragma unroll
     for (int u = 0; u < KU; ++u) {
       const int unit = tid + u * kThreads;
       // A thread without a piece reads past every buffer range (zeros).
@@ -356,7 +357,7 @@ void fa_fwd_bf16_kernel(Params p) {
     bool v_unit[VU];
     int vkg[VU], vdc[VU];
     uint32_t v_off[VU];
-  #pragma unroll
+#pragma unroll
     for (int u = 0; u < VU; ++u) {
       const int unit = tid + u * kThreads;
       v_unit[u] = unit < VUNITS;
@@ -367,30 +368,32 @@ void fa_fwd_bf16_kernel(Params p) {
     u32x4_t kreg[KU], vreg[VU][4];
     auto load_block = [&](int j) {
       const int kbase = j * BN;
-      const rsrc_t rk = make_rsrc(Kh + (size_t)kbase * (KRB / 2), (uint32_t)max(0, Nk - kbase) * KRB);
-      const rsrc_t rv = make_rsrc(Vh + (size_t)kbase * (VRB / 2), (uint32_t)max(0, n_vis - kbase) * VRB);
-  #pragma unroll
+      const rsrc_t rk =
+          make_rsrc(Kh + (size_t)kbase * (KRB / 2), (uint32_t)max(0, Nk - kbase) * KRB);
+      const rsrc_t rv =
+          make_rsrc(Vh + (size_t)kbase * (VRB / 2), (uint32_t)max(0, n_vis - kbase) * VRB);
+#pragma unroll
       for (int u = 0; u < KU; ++u) kreg[u] = buf_load16(rk, k_off[u]);
-  #pragma unroll
+#pragma unroll
       for (int u = 0; u < VU; ++u) {
         if (v_unit[u]) {
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < 4; ++i) vreg[u][i] = buf_load16(rv, v_off[u] + i * VRB);
         }
       }
     };
     auto store_block = [&](int buf) {
-  #pragma unroll
+#pragma unroll
       for (int u = 0; u < KU; ++u) {
         const int unit = tid + u * kThreads;
         if (KFULL || unit < KUNITS) *(u32x4_t*)&k_lds[buf][unit / CPR][8 * (unit % CPR)] = kreg[u];
       }
-  #pragma unroll
+#pragma unroll
       for (int u = 0; u < VU; ++u) {
         if (v_unit[u]) {
           // Dword w of key i holds dims 8*vdc + 2w, +1: regroup into
           // (keys 0-3 of dim 2w) and (keys 0-3 of dim 2w+1).
-  #pragma unroll
+#pragma unroll
           for (int w = 0; w < 4; ++w) {
             const unsigned a0 = vreg[u][0][w], a1 = vreg[u][1][w], a2 = vreg[u][2][w],
                            a3 = vreg[u][3][w];
@@ -409,9 +412,9 @@ void fa_fwd_bf16_kernel(Params p) {
     float l_run = 0.f;         // row sum of the bf16-rounded probabilities (normalises O)
     float le_run = 0.f;        // row sum of the fp32 probabilities (gives LSE)
     f32x16_t acc[DT];
-  #pragma unroll
+#pragma unroll
     for (int dt = 0; dt < DT; ++dt)
-  #pragma unroll
+#pragma unroll
       for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
     const float c = p.c;
     const int krow = k_row_perm(n);
@@ -423,10 +426,10 @@ void fa_fwd_bf16_kernel(Params p) {
     auto exps = [&](const f32x16_t (&s)[KT], u32x4_t (&pb)[PC], float base, float& re,
                     float& rs) {
       float re0 = 0.f, re1 = 0.f, rs0 = 0.f, rs1 = 0.f;
-  #pragma unroll
+#pragma unroll
       for (int pc = 0; pc < PC; ++pc) {
         const int kt = pc >> 1, r0 = 8 * (pc & 1);
-  #pragma unroll
+#pragma unroll
         for (int w = 0; w < 4; ++w) {
           const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r0 + 2 * w], c, -base));
           const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r0 + 2 * w + 1], c, -base));
@@ -457,13 +460,13 @@ void fa_fwd_bf16_kernel(Params p) {
       if (!wave_skip) {
         // S^T = K_j Q^T with K rows permuted (row 32kt + krow feeds MFMA row n).
         f32x16_t s[KT];
-  #pragma unroll
+#pragma unroll
         for (int kt = 0; kt < KT; ++kt)
-  #pragma unroll
+#pragma unroll
           for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-  #pragma unroll
+#pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-  #pragma unroll
+#pragma unroll
           for (int kt = 0; kt < KT; ++kt) {
             const u32x4_t a = *(const u32x4_t*)&k_lds[buf][32 * kt + krow][16 * ks + 8 * hf];
             s[kt] = mfma_bf16(a, qr[ks], s[kt]);
@@ -473,7 +476,7 @@ void fa_fwd_bf16_kernel(Params p) {
         // softmax runs.
         constexpr int VPRE = FA_V_PREFETCH < PC * DT ? FA_V_PREFETCH : PC * DT;
         u32x4_t vpre[VPRE > 0 ? VPRE : 1];
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < VPRE; ++i)
           vpre[i] = *(const u32x4_t*)&vt_lds[buf][32 * (i % DT) + n][16 * (i / DT) + 8 * hf];
         // Register r of key tile kt holds key kbase + 32kt + 16(r/8) + 8hf + r%8.
@@ -482,9 +485,9 @@ void fa_fwd_bf16_kernel(Params p) {
           const int qrow = qw0 + n;
           const int lim = (causal ? min(qrow + off, n_vis - 1) : n_vis - 1) - kbase - 8 * hf;
           const int lim_lo = (W >= 0) ? qrow + off - W - kbase - 8 * hf : -BN;
-  #pragma unroll
+#pragma unroll
           for (int kt = 0; kt < KT; ++kt)
-  #pragma unroll
+#pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int idx = 32 * kt + 16 * (r >> 3) + (r & 7);
               if (idx > lim || idx < lim_lo) s[kt][r] = -INFINITY;
@@ -504,15 +507,15 @@ void fa_fwd_bf16_kernel(Params p) {
         }
         if (full) {
           float mx = s[0][0];
-  #pragma unroll
+#pragma unroll
           for (int kt = 0; kt < KT; ++kt)
-  #pragma unroll
+#pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
           const float m_new = fmaxf(m_run, pair_max(mx) * c);
           const float alpha = (m_new == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-  #pragma unroll
+#pragma unroll
           for (int dt = 0; dt < DT; ++dt)
-  #pragma unroll
+#pragma unroll
             for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
           l_run *= alpha;
           le_run *= alpha;
@@ -524,16 +527,18 @@ void fa_fwd_bf16_kernel(Params p) {
         le_run += re;
 
         // O^T += V_j^T P^T: A operand = V^T rows 32dt + n, keys 16pc + 8hf + 0..7.
-  #pragma unroll
+#pragma unroll
         for (int pc = 0; pc < PC; ++pc)
-  #pragma unroll
+#pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
             const int i = pc * DT + dt;
-            const u32x4_t a = i < VPRE ? vpre[i < VPRE ? i : 0]
-                                       : *(const u32x4_t*)&vt_lds[buf][32 * dt + n][16 * pc + 8 * hf];
+            const u32x4_t a =
+                i < VPRE ? vpre[i < VPRE ? i : 0]
+                         : *(const u32x4_t*)&vt_lds[buf][32 * dt + n][16 * pc + 8 * hf];
             acc[dt] = mfma_bf16(a, pb[pc], acc[dt]);
           }
-        mfma_read_ahead<PC * DT, (PC * DT - VPRE < FA_READ_AHEAD ? PC * DT - VPRE : FA_READ_AHEAD)>();
+        constexpr int VREST = PC * DT - VPRE;   // V^T operands read inside the P V loop
+        mfma_read_ahead<PC * DT, (VREST < FA_READ_AHEAD ? VREST : FA_READ_AHEAD)>();
       }
       if (more) store_block(buf ^ 1);
       __syncthreads();
@@ -549,9 +554,9 @@ void fa_fwd_bf16_kernel(Params p) {
     const int qrow = qw0 + n;
     if (qrow < N) {
       uint16_t* orow = Oh + (size_t)qrow * (GEN ? (size_t)p.ors : (size_t)D);
-  #pragma unroll
+#pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-  #pragma unroll
+#pragma unroll
         for (int a = 0; a < 4; ++a) {
           u32x2_t x = {pack_bf16(acc[dt][4 * a] * inv, acc[dt][4 * a + 1] * inv),
                        pack_bf16(acc[dt][4 * a + 2] * inv, acc[dt][4 * a + 3] * inv)};
