@@ -67,6 +67,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "fa_api.h"
 
@@ -759,22 +760,25 @@ constexpr long long kCUs = 256;   // compute units of an MI355X
 
 // One bf16 forward launch: 8-wave (256-row) workgroups when big, else 4-wave.
 // Workgroups of one kernel instantiation that the chip holds at once
-// (occupancy per compute unit x compute units), queried once.
+// (occupancy per compute unit x compute units).  The first successful query
+// is cached; while the runtime cannot answer (it only sets the grid size),
+// one workgroup per compute unit is assumed and nothing is cached.
 template <int D, int NW, int MODE>
 long long resident_workgroups() {
-  static const long long n = [] {
-    int occ = 0, dev = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fa_fwd_bf16_kernel<D, NW, MODE>,
-                                                     64 * NW, 0) != hipSuccess || occ < 1)
-      occ = 1;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus < 1)
-      cus = (int)kCUs;
-    (void)hipGetLastError();   // a failed query only changes the grid size
-    return (long long)occ * cus;
-  }();
-  return n;
+  static std::atomic<long long> cached{0};
+  const long long known = cached.load(std::memory_order_relaxed);
+  if (known > 0) return known;
+  int occ = 0, dev = 0, cus = 0;
+  const bool ok =
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fa_fwd_bf16_kernel<D, NW, MODE>,
+                                                   64 * NW, 0) == hipSuccess &&
+      occ > 0 && hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      cus > 0;
+  (void)hipGetLastError();   // a failed query is not the caller's error
+  if (!ok) return kCUs;
+  cached.store((long long)occ * cus, std::memory_order_relaxed);
+  return (long long)occ * cus;
 }
 
 // One launch over p.items work items.  Contiguous self-attention with

@@ -43,10 +43,9 @@
  *    one kernel on it and returns without synchronising.
  *
  * Ownership and side effects: the caller owns every buffer; the library
- * allocates no memory.  Its only state is a process-wide, read-only cache
- * of how many workgroups of each forward kernel the device holds at once
- * (an occupancy query made on a kernel's first launch; it sets the grid
- * size only).  It writes o and lse and nothing else.  Inputs are only
+ * allocates no memory.  Its only state is a process-wide cache of how many
+ * workgroups of each forward kernel the device holds at once (the first
+ * occupancy query that succeeds; it sets the grid size only).  It writes o and lse and nothing else.  Inputs are only
  * read.
  *
  * Errors: every argument is checked on the host before anything is
