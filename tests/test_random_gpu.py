@@ -149,3 +149,21 @@ def test_grids_larger_than_the_chip(B, H, N, d, mask):
     ref = attention_general_ref(to_f64(x["q"]), to_f64(x["k"]), to_f64(x["v"]), scale, mask, -1,
                                 x.get("kv_lens"), magnitudes=True)
     compare_bound(O, L, ref, what)
+
+
+@pytest.mark.parametrize("d,mask", [(64, MASK_KEY_PADDING), (128, MASK_KEY_PADDING | 1)])
+def test_looping_workgroups_with_empty_and_edge_key_lengths(d, mask):
+    """Items without any visible key (kv_len = 0) and key lengths at block
+    edges inside a grid larger than the chip: looping workgroups must skip
+    the empty items' key loop, write O = 0 and LSE = -inf for them, and keep
+    their LDS buffers consistent for the next item."""
+    B, H, N = 9, 32, 600
+    x = make_raw(B, H, N, d, "bf16", seed=4242 + d, q_mult=2.0, kv_len_range=(1, N))
+    x["kv_lens"] = np.array([0, 1, 64, 128, 0, N, 129, 0, 383], dtype=np.int32)
+    scale = d ** -0.5
+    what = f"fa_fwd B={B} H={H} N={N} d={d} mask={mask} kv={x['kv_lens'].tolist()}"
+    say(what)
+    O, L = _run(x, scale, mask, -1, "bhnd", True)
+    ref = attention_general_ref(to_f64(x["q"]), to_f64(x["k"]), to_f64(x["v"]), scale, mask, -1,
+                                x["kv_lens"], magnitudes=True)
+    compare_bound(O, L, ref, what)
