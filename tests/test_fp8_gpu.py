@@ -195,3 +195,42 @@ def test_errors_write_nothing():
     assert e.value.status == fa.FA_ERR_UNSUPPORTED
     torch.cuda.synchronize()
     assert torch.isnan(o.float()).all() and torch.isnan(lse).all()
+
+
+FP8_EDGES = [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 383, 511, 513]
+
+
+@pytest.mark.parametrize("chunk", range(3))
+def test_random_shapes_masks_and_scales(chunk):
+    """Seeded random cases: each draws d, B, H, N (half of them at the 64-,
+    128- and 256-row block edges), the mask, the key lengths and the scale
+    from its own seed, so a failure names a reproducible case."""
+    for seed in range(700 + 12 * chunk, 700 + 12 * chunk + 12):
+        rng = np.random.default_rng(seed)
+        d = int(rng.choice([64, 128]))
+        B, H = int(rng.integers(1, 4)), int(rng.integers(1, 6))
+        N = int(rng.choice(FP8_EDGES)) if rng.random() < 0.5 else int(rng.integers(1, 1200))
+        mask = int(rng.integers(0, 4))
+        scale = float(d ** -0.5 * rng.choice([1.0, 1.0, -0.7, 2.5]))
+        kv_range = (0, N) if mask & MASK_KEY_PADDING else None
+        what = f"seed={seed} B={B} H={H} N={N} d={d} mask={mask} scale={scale:.4f}"
+        say(what)
+        x = make_raw(B, H, N, d, "fp8", seed=seed, q_mult=2.0, kv_len_range=kv_range)
+        O, L = run_fp8(x, scale, mask)
+        compare_fp8(O, L, oracle(x, scale, mask), what)
+
+
+@pytest.mark.parametrize("B,H,N,d,mask", [
+    (4, 37, 1100, 128, MASK_KEY_PADDING | MASK_CAUSAL),   # 8-wave blocks, 8 does not divide B*H
+    (2, 48, 1536, 64, MASK_CAUSAL),                       # 8-wave blocks, heads split over XCDs
+    (3, 40, 900, 128, MASK_KEY_PADDING),
+])
+def test_grids_larger_than_the_chip(B, H, N, d, mask):
+    """More workgroups than the chip holds at once, with and without a head
+    count that divides by the XCD count, on every element."""
+    kv_range = (1, N) if mask & MASK_KEY_PADDING else None
+    x = make_raw(B, H, N, d, "fp8", seed=B * 100 + H + N + d, q_mult=2.0, kv_len_range=kv_range)
+    what = f"B={B} H={H} N={N} d={d} mask={mask}"
+    say(what)
+    O, L = run_fp8(x, d ** -0.5, mask)
+    compare_fp8(O, L, oracle(x, d ** -0.5, mask), what, bulk=True)
