@@ -18,7 +18,7 @@ Names follow the C ABI of ``include/fa_api.h``:
   mask_kind=0, kv_lens=None, stream=None)`` -- E4M3 codes (uint8 tensors)
   with per-(batch, head) float32 scales; o is bf16
 * ``fa_decode_paged(q, k_pool, v_pool, block_tables, seq_lens, o, lse,
-  workspace, scale, num_blocks=None, stream=None)`` and
+  workspace, scale, stream=None)`` and
   ``fa_decode_paged_workspace_bytes(B, H, d, block_size, max_blocks)``
 * ``fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, dp_rowsum, scale, mask_kind=0,
   kv_lens=None, stream=None)`` -- bf16 gradients
@@ -96,30 +96,44 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _check(nm, t, dtype, shape=None, device=None, contiguous=True):
+    """Raise unless t is a tensor of ``dtype`` in device memory (on ``device``
+    when given), contiguous unless told otherwise, of ``shape`` when given.
+    Every pointer the library receives passes through here, so no host
+    pointer, overlapping view or zero-stride expansion reaches a kernel."""
+    import torch
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype:
+        raise TypeError(f"{nm} must be a {dtype} tensor, got {getattr(t, 'dtype', type(t))}")
+    if not t.is_cuda:
+        raise ValueError(f"{nm} must be in device memory")
+    if device is not None and t.device != device:
+        raise ValueError(f"{nm} is on {t.device}, the other tensors on {device}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{nm} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{nm} must be {list(shape)}, got {list(t.shape)}")
+
+
+def _check_kv_lens(kv_lens, B, device):
+    import torch
+    if kv_lens is not None:
+        _check("kv_lens", kv_lens, torch.int32, (B,), device)
+
+
 def _call(name, q, k, v, o, lse, scale, mask_kind, kv_lens, stream, dtype):
     import torch
     lib = load_library()
-    for nm, t in (("q", q), ("k", k), ("v", v), ("o", o)):
-        if t.dtype != dtype:
-            raise TypeError(f"{nm} must be {dtype}, got {t.dtype}")
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{nm} must be a contiguous device tensor")
-        if t.dim() != 4 or t.shape != q.shape:
-            raise ValueError(f"{nm} must have the shape of q, [B, H, N, d]")
+    _check("q", q, dtype)
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B, H, N, d], got {list(q.shape)}")
+    for nm, t in (("k", k), ("v", v), ("o", o)):
+        _check(nm, t, dtype, q.shape, q.device)
     B, H, N, d = q.shape
-    if lse.dtype != torch.float32 or not lse.is_cuda or not lse.is_contiguous() \
-            or tuple(lse.shape) != (B, H, N):
-        raise ValueError("lse must be a contiguous float32 device tensor [B, H, N]")
-    if kv_lens is not None:
-        if kv_lens.dtype != torch.int32 or not kv_lens.is_cuda or kv_lens.numel() != B:
-            raise ValueError("kv_lens must be an int32 device tensor [B]")
-    if stream is None:
-        stream = torch.cuda.current_stream(q.device).cuda_stream
-    elif not isinstance(stream, int):
-        stream = stream.cuda_stream
+    _check("lse", lse, torch.float32, (B, H, N), q.device)
+    _check_kv_lens(kv_lens, B, q.device)
     st = getattr(lib, name)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
                             float(scale), int(mask_kind), _ptr(kv_lens),
-                            ctypes.c_void_p(stream))
+                            ctypes.c_void_p(_stream_handle(stream, q.device)))
     if st != FA_OK:
         raise FaError(st, fa_strerror(st))
 
@@ -150,19 +164,20 @@ def fa_fwd_general(q, k, v, o, lse, scale, mask_kind=FA_MASK_NONE, window_left=-
     dimension is contiguous); lse contiguous float32 [B, H, Nq]."""
     import torch
     lib = load_library()
+    _check("q", q, torch.bfloat16, contiguous=False)
+    _check("k", k, torch.bfloat16, device=q.device, contiguous=False)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [B, H, Nq, d] and [B, H, Nk, d]")
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
     strides = []
     for nm, t, rows in (("q", q, Nq), ("k", k, Nk), ("v", v, Nk), ("o", o, Nq)):
-        if t.dtype != torch.bfloat16 or not t.is_cuda:
-            raise TypeError(f"{nm} must be a bf16 device tensor")
-        if tuple(t.shape) != (B, H, rows, d) or t.stride(3) != 1:
-            raise ValueError(f"{nm} must be [B, H, {rows}, d] with a contiguous last dimension")
+        _check(nm, t, torch.bfloat16, (B, H, rows, d), q.device, contiguous=False)
+        if t.stride(3) != 1:
+            raise ValueError(f"{nm} must have a contiguous last dimension")
         strides.append((ctypes.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2)))
-    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, H, Nq):
-        raise ValueError("lse must be a contiguous float32 device tensor [B, H, Nq]")
-    if kv_lens is not None and (kv_lens.dtype != torch.int32 or kv_lens.numel() != B):
-        raise ValueError("kv_lens must be an int32 device tensor [B]")
+    _check("lse", lse, torch.float32, (B, H, Nq), q.device)
+    _check_kv_lens(kv_lens, B, q.device)
     st = lib.fa_fwd_general(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d,
                             *[ctypes.cast(a, ctypes.c_void_p) for a in strides], float(scale),
                             int(mask_kind), int(window_left), _ptr(kv_lens),
@@ -178,19 +193,20 @@ def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, sca
     int32 device tensors [B + 1] of sequence boundaries."""
     import torch
     lib = load_library()
+    _check("q", q, torch.bfloat16)
+    _check("k", k, torch.bfloat16, device=q.device)
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q and k must be [total_q, H, d] and [total_k, H, d]")
     total_q, H, d = q.shape
     total_k = k.shape[0]
     for nm, t, rows in (("q", q, total_q), ("k", k, total_k), ("v", v, total_k),
                         ("o", o, total_q)):
-        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
-            raise TypeError(f"{nm} must be a contiguous bf16 device tensor")
-        if tuple(t.shape) != (rows, H, d):
-            raise ValueError(f"{nm} must be [{rows}, H, d]")
-    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (H, total_q):
-        raise ValueError("lse must be a contiguous float32 device tensor [H, total_q]")
+        _check(nm, t, torch.bfloat16, (rows, H, d), q.device)
+    _check("lse", lse, torch.float32, (H, total_q), q.device)
     for nm, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
-        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous() or t.dim() != 1:
-            raise ValueError(f"{nm} must be a contiguous int32 device tensor [B + 1]")
+        _check(nm, t, torch.int32, device=q.device)
+        if t.dim() != 1:
+            raise ValueError(f"{nm} must be [B + 1]")
     B = cu_seqlens_q.numel() - 1
     if B < 1 or cu_seqlens_k.numel() != B + 1:
         raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B + 1 >= 2 entries")
@@ -208,25 +224,19 @@ def fa_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, o, lse, scale, mask_kin
     writes o (bf16) and lse (float32)."""
     import torch
     lib = load_library()
-    for nm, t in (("q", q), ("k", k), ("v", v)):
-        if t.dtype != torch.uint8:
-            raise TypeError(f"{nm} must hold E4M3 codes as torch.uint8, got {t.dtype}")
-        if not t.is_cuda or not t.is_contiguous() or t.dim() != 4 or t.shape != q.shape:
-            raise ValueError(f"{nm} must be a contiguous device tensor shaped like q")
+    _check("q", q, torch.uint8)    # E4M3 codes
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B, H, N, d], got {list(q.shape)}")
+    for nm, t in (("k", k), ("v", v)):
+        _check(nm, t, torch.uint8, q.shape, q.device)
     B, H, N, d = q.shape
     for nm, t in (("q_descale", q_descale), ("k_descale", k_descale), ("v_descale", v_descale)):
-        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() \
-                or t.numel() != B * H:
-            raise ValueError(f"{nm} must be a contiguous float32 device tensor [B, H]")
-    if o.dtype != torch.bfloat16 or not o.is_cuda or not o.is_contiguous() \
-            or tuple(o.shape) != (B, H, N, d):
-        raise ValueError("o must be a contiguous bf16 device tensor [B, H, N, d]")
-    if lse.dtype != torch.float32 or not lse.is_cuda or not lse.is_contiguous() \
-            or tuple(lse.shape) != (B, H, N):
-        raise ValueError("lse must be a contiguous float32 device tensor [B, H, N]")
-    if kv_lens is not None:
-        if kv_lens.dtype != torch.int32 or not kv_lens.is_cuda or kv_lens.numel() != B:
-            raise ValueError("kv_lens must be an int32 device tensor [B]")
+        _check(nm, t, torch.float32, device=q.device)
+        if t.numel() != B * H:
+            raise ValueError(f"{nm} must hold B * H = {B * H} scales")
+    _check("o", o, torch.bfloat16, (B, H, N, d), q.device)
+    _check("lse", lse, torch.float32, (B, H, N), q.device)
+    _check_kv_lens(kv_lens, B, q.device)
     st = lib.fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(q_descale), _ptr(k_descale),
                         _ptr(v_descale), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
                         int(mask_kind), _ptr(kv_lens),
@@ -246,24 +256,25 @@ def fa_decode_paged(q, k_pool, v_pool, block_tables, seq_lens, o, lse, workspace
     seq_lens int32 [B]; writes o (bf16 [B, H, d]) and lse (float32 [B, H])."""
     import torch
     lib = load_library()
+    _check("q", q, torch.bfloat16)
+    _check("k_pool", k_pool, torch.bfloat16, device=q.device)
+    if q.dim() != 3 or k_pool.dim() != 4:
+        raise ValueError("q must be [B, H, d] and the pools [num_blocks, H, block_size, d]")
     B, H, d = q.shape
     nblk, Hp, bs, dp = k_pool.shape
-    for nm, t in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool), ("o", o)):
-        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{nm} must be a contiguous bf16 device tensor")
-    if v_pool.shape != k_pool.shape or Hp != H or dp != d or tuple(o.shape) != (B, H, d):
-        raise ValueError("pools must be [num_blocks, H, block_size, d] and o [B, H, d]")
-    for nm, t, shp in (("block_tables", block_tables, None), ("seq_lens", seq_lens, (B,))):
-        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{nm} must be a contiguous int32 device tensor")
-    if block_tables.dim() != 2 or block_tables.shape[0] != B or tuple(seq_lens.shape) != (B,):
-        raise ValueError("block_tables must be [B, max_blocks] and seq_lens [B]")
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H) or not lse.is_cuda:
-        raise ValueError("lse must be a float32 device tensor [B, H]")
+    if Hp != H or dp != d:
+        raise ValueError("pools must be [num_blocks, H, block_size, d] with q's H and d")
+    _check("v_pool", v_pool, torch.bfloat16, k_pool.shape, q.device)
+    _check("o", o, torch.bfloat16, (B, H, d), q.device)
+    _check("block_tables", block_tables, torch.int32, device=q.device)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B, max_blocks]")
+    _check("seq_lens", seq_lens, torch.int32, (B,), q.device)
+    _check("lse", lse, torch.float32, (B, H), q.device)
     need = fa_decode_paged_workspace_bytes(B, H, d, bs, block_tables.shape[1])
-    if workspace.dtype != torch.float32 or not workspace.is_cuda \
-            or workspace.numel() * 4 < need:
-        raise ValueError(f"workspace must be a float32 device tensor of >= {need} bytes")
+    _check("workspace", workspace, torch.float32, device=q.device)
+    if workspace.numel() * 4 < need:
+        raise ValueError(f"workspace must hold >= {need} bytes")
     st = lib.fa_decode_paged(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
                              _ptr(seq_lens), _ptr(o), _ptr(lse), _ptr(workspace), B, H, d, bs,
                              block_tables.shape[1], nblk, float(scale),
@@ -277,22 +288,16 @@ def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, dp_rowsum, scale, mask_kind=FA_MAS
     """bf16 backward: writes dq, dk, dv (bf16) and dp_rowsum (float32 [B, H, N])."""
     import torch
     lib = load_library()
-    for nm, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq),
-                  ("dk", dk), ("dv", dv)):
-        if t.dtype != torch.bfloat16:
-            raise TypeError(f"{nm} must be torch.bfloat16, got {t.dtype}")
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{nm} must be a contiguous device tensor")
-        if t.dim() != 4 or t.shape != q.shape:
-            raise ValueError(f"{nm} must have the shape of q, [B, H, N, d]")
+    _check("q", q, torch.bfloat16)
+    if q.dim() != 4:
+        raise ValueError(f"q must be [B, H, N, d], got {list(q.shape)}")
+    for nm, t in (("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk),
+                  ("dv", dv)):
+        _check(nm, t, torch.bfloat16, q.shape, q.device)
     B, H, N, d = q.shape
     for nm, t in (("lse", lse), ("dp_rowsum", dp_rowsum)):
-        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() \
-                or tuple(t.shape) != (B, H, N):
-            raise ValueError(f"{nm} must be a contiguous float32 device tensor [B, H, N]")
-    if kv_lens is not None:
-        if kv_lens.dtype != torch.int32 or not kv_lens.is_cuda or kv_lens.numel() != B:
-            raise ValueError("kv_lens must be an int32 device tensor [B]")
+        _check(nm, t, torch.float32, (B, H, N), q.device)
+    _check_kv_lens(kv_lens, B, q.device)
     st = lib.fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
                     _ptr(dk), _ptr(dv), _ptr(dp_rowsum), B, H, N, d, float(scale),
                     int(mask_kind), _ptr(kv_lens),
