@@ -408,8 +408,6 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   constexpr int BQ = 64;             // query rows per block
   constexpr int KS = D / 16;         // k-steps over d
   constexpr int DT = D / 32;         // 32-row tiles of dK^T, dV^T
-  constexpr int QT = BQ / 32;        // 32-query tiles of S, dP
-  constexpr int PC = BQ / 16;        // 16-query chunks of P, dS
   constexpr int RLD = D + 8;
   constexpr int TLD = BQ + 8;
   constexpr uint32_t ROWB = D * 2;
