@@ -27,7 +27,11 @@
  *    scaled logits.  A query row with no visible key gets O = 0 and
  *    LSE = -inf.
  *  - B, H, N >= 1; d is 32, 64, 96, 128 or 256 for fa_fwd, 64 or 128 for
- *    fa_fwd_f32.  B * H * ceil(N / 128) must not exceed 2^31 - 1.
+ *    fa_fwd_f32.  B * H * ceil(N / 128) must not exceed 2^31 - 1, and
+ *    (N + 256) * d * 4 (fa_fwd; N + 128 for fa_fwd_f32) must not exceed
+ *    2^32 - 1: one head's rows, plus one block past the end, are addressed
+ *    with 32-bit byte offsets.  So N <= 16776959 at d = 64 and 8388351 at
+ *    d = 128 for fa_fwd.
  *  - scale: any finite float; the logits are scale * q.k.  (1/sqrt(d) is the
  *    usual value.)  |scale| below 1e-30 is treated as 1e-30, which gives the
  *    same uniform softmax as scale = 0 to within float32 rounding.
@@ -109,7 +113,10 @@ int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, float* lse,
  *    c < kv_len (key padding), c <= a_r (FA_MASK_CAUSAL), and
  *    c >= a_r - window_left when window_left >= 0 (window_left = -1: no
  *    window).  A row that sees no key gets O = 0, LSE = -inf.
- *  - Nq, Nk >= 1; d is 32, 64, 96, 128 or 256; 16-byte aligned pointers; other
+ *  - Nq, Nk >= 1; d is 32, 64, 96, 128 or 256; 16-byte aligned pointers.
+ *    B * H * ceil(Nq / 128) must not exceed 2^31 - 1, and for each tensor
+ *    (rows + 256) * row_stride * 2 must not exceed 2^32 - 1 (rows = Nq for
+ *    q and o, Nk for k and v): a head's rows use 32-bit byte offsets.  Other
  *    conventions (scale, kv_lens, stream, errors) as for fa_fwd.  With
  *    contiguous strides, Nq = Nk and no window it computes exactly fa_fwd. */
 int fa_fwd_general(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -135,8 +142,9 @@ int fa_fwd_general(const void* q, const void* k, const void* v, void* o, float* 
  *  - max_seqlen_q must be at least every Nq_b: rows past it are not
  *    written.  mask_kind: FA_MASK_NONE or FA_MASK_CAUSAL (key lengths come
  *    from cu_seqlens_k).  A sequence with Nk_b = 0 gets O = 0, LSE = -inf.
- *  - total_q = 0 or max_seqlen_q = 0 enqueues nothing.  Other conventions
- *    (d, scale, stream, errors) as for fa_fwd_general. */
+ *  - total_q = 0 or max_seqlen_q = 0 enqueues nothing.  (total_q + 256) *
+ *    H * d * 2 and (total_k + 256) * H * d * 2 must not exceed 2^32 - 1.
+ *    Other conventions (d, scale, stream, errors) as for fa_fwd_general. */
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B, int H,
                   int d, int64_t total_q, int64_t total_k, int max_seqlen_q, float scale,
@@ -151,10 +159,12 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
  * those values, with the same mask, scale, LSE and empty-row conventions as
  * fa_fwd; o is bfloat16 [B, H, N, d], lse float32 [B, H, N].
  *  - Products run on the E4M3 matrix cores with float32 accumulation.  The
- *    probabilities (each at most 1: the row max is exact) are multiplied by
- *    448 and rounded to E4M3 before they multiply V; the factor cancels in
- *    the normalisation.  Rounding P to E4M3 (relative error up to 2^-4) is
- *    the dominant error of this path.
+ *    probabilities are taken against a reference max that lags the row max
+ *    by at most 2 binary orders (so each is at most 4), multiplied by 448/4
+ *    and rounded to E4M3 before they multiply V; the factor cancels in the
+ *    normalisation, which divides by the float32 sum of the unrounded
+ *    values.  Rounding P to E4M3 (relative error up to 2^-4) is the
+ *    dominant error of this path.
  *  - q_descale, k_descale, v_descale: DEVICE pointers to float32 [B * H],
  *    4-byte aligned, finite and positive (not checked on the host).
  *  - Everything else as for fa_fwd. */
@@ -185,7 +195,8 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, const float* q_desca
  *    kernels the call enqueues (calls that share a workspace must not
  *    overlap).
  *  - d is 64 or 128; block_size a multiple of 8 (8 .. 65536); any finite
- *    scale; B, H <= 65535.  Errors as for fa_fwd.  The library allocates
+ *    scale; B, H <= 65535; block_size * max_blocks_per_seq <= 2^31 - 1.
+ *    Errors as for fa_fwd.  The library allocates
  *    nothing. */
 size_t fa_decode_paged_workspace_bytes(int B, int H, int d, int block_size,
                                        int max_blocks_per_seq);

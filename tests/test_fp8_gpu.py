@@ -234,3 +234,47 @@ def test_grids_larger_than_the_chip(B, H, N, d, mask):
     say(what)
     O, L = run_fp8(x, d ** -0.5, mask)
     compare_fp8(O, L, oracle(x, d ** -0.5, mask), what, bulk=True)
+
+
+def test_largest_n():
+    """N at the entry point's bound ((N + 256) d 4 <= 2^32 - 1) with key
+    padding to 200 keys: sampled rows through the last block against the
+    oracle, every output written, one row more refused.  Inputs are drawn
+    on the device; the sampled query rows are placed first in a 200-row
+    query block for the oracle (unmasked rows are independent)."""
+    import torch
+
+    import exact_attention_92_amd as fa
+    d, KV = 128, 200
+    N = (2 ** 32 - 1) // (d * 4) - 256
+    assert (N + 257) * d * 4 > 2 ** 32 - 1
+    say(f"[fp8 largest N] N={N} d={d} key padding {KV}")
+    g = torch.Generator(device="cuda").manual_seed(31)
+    q, k, v = (torch.randn((1, 1, N, d), generator=g, device="cuda").to(torch.float8_e4m3fn)
+               .view(torch.uint8) for _ in range(3))
+    ds = torch.ones((1, 1), device="cuda")
+    o = torch.full((1, 1, N, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((1, 1, N), float("nan"), device="cuda")
+    kv = torch.tensor([KV], dtype=torch.int32, device="cuda")
+    scale = d ** -0.5
+    fa.fa_fwd_fp8(q, k, v, ds, ds, ds, o, lse, scale, MASK_KEY_PADDING, kv)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o).any().item() and torch.isfinite(lse).all().item()
+    rows = np.array(sorted({0, 1, 127, 128, 255, 256, N // 2, N - 257, N - 256, N - 129, N - 128,
+                            N - 65, N - 2, N - 1}))
+    qs = np.zeros((1, 1, KV, d), dtype=np.uint8)
+    qs[:, :, :len(rows)] = q[:, :, rows].cpu().numpy()
+    one = np.ones((1, 1), dtype=np.float32)
+    x = {"q": qs, "k": k[:, :, :KV].cpu().numpy(), "v": v[:, :, :KV].cpu().numpy(),
+         "kv_lens": None, "q_descale": one, "k_descale": one, "v_descale": one}
+    ref = oracle(x, scale, MASK_NONE, rows=np.arange(len(rows)))
+    O = o_to_f64(o[:, :, rows])
+    L = lse[:, :, rows].cpu().numpy().astype(np.float64)
+    st = fa.load_library().fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), ds.data_ptr(),
+                                      ds.data_ptr(), ds.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                      1, 1, N + 1, d, scale, MASK_KEY_PADDING, kv.data_ptr(),
+                                      torch.cuda.current_stream().cuda_stream)
+    assert st == fa.FA_ERR_INVALID_ARG
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    compare_fp8(O, L, ref, f"largest N={N}")
