@@ -51,6 +51,12 @@ def _f64(t):
     return t.float().cpu().numpy().astype(np.float64)
 
 
+def _at(t, rows):
+    """Rows ``rows`` (numpy indices) of a [1, 1, N, ...] device tensor."""
+    import torch
+    return t[:, :, torch.as_tensor(rows, device=t.device)]
+
+
 def _stream():
     import torch
     return torch.cuda.current_stream().cuda_stream
@@ -136,6 +142,111 @@ def test_fa_fwd_general_largest_n_windowed():
     st = lib.fa_fwd_general(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                             lse.data_ptr(), 1, 1, N + 1, N + 1, d, None, None, None, None, scale,
                             MASK_CAUSAL, WINDOW, None, _stream())
+    assert st == fa.FA_ERR_INVALID_ARG
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    compare_bound(O, L, ref, what)
+
+
+def test_fa_bwd_largest_n():
+    """The backward at its bound ((N + 256) d 4 <= 2^32 - 1) with key padding
+    to 200 keys.  dQ and the row sums on sampled rows against the oracle
+    (the sampled rows placed first in a 200-row query block: unmasked rows
+    are independent); keys no row sees have dK = dV = 0 exactly; over the
+    visible keys every row's dS sums to 0 and P to 1, so sum_c dK_c = 0 and
+    sum_c dV_c = sum_r dO_r."""
+    import torch
+
+    import exact_attention_92_amd as fa
+    from gpu_util import compare_grads
+    from oracle import attention_bwd_ref
+    d = 64
+    N = LIMIT // (d * 4) - 256
+    what = f"fa_bwd B=1 H=1 N={N} d={d} key padding {KV}"
+    say(what)
+    q, k, v, do = (_draw((1, 1, N, d), torch.bfloat16, s) for s in (31, 32, 33, 34))
+    kv = torch.tensor([KV], dtype=torch.int32, device="cuda")
+    scale = d ** -0.5
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 1, N), device="cuda")
+    fa.fa_fwd(q, k, v, o, lse, scale, MASK_KEY_PADDING, kv)
+    dq, dk, dv = (torch.full_like(q, float("nan")) for _ in range(3))
+    dps = torch.full((1, 1, N), float("nan"), device="cuda")
+    fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, dps, scale, MASK_KEY_PADDING, kv)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv, dps):
+        assert not torch.isnan(t).any().item()
+    assert (dk[:, :, KV:] == 0).all().item() and (dv[:, :, KV:] == 0).all().item()
+    dv_sum = dv[:, :, :KV].double().sum(dim=2)
+    do_sum = do.double().sum(dim=2)
+    assert (dv_sum - do_sum).abs().max().item() <= 2e-2 * N ** 0.5, "sum dV"
+    dk_vis = dk[:, :, :KV].double()
+    assert (dk_vis.sum(dim=2).abs() <= 1e-2 * dk_vis.abs().sum(dim=2)).all().item(), "sum dK"
+    rows = _rows(N, d * 2)
+    R = len(rows)
+    qs, dos = np.zeros((1, 1, KV, d)), np.zeros((1, 1, KV, d))
+    qs[:, :, :R], dos[:, :, :R] = _f64(_at(q, rows)), _f64(_at(do, rows))
+    dQ, _, _, DP, M = attention_bwd_ref(qs, _f64(k[:, :, :KV]), _f64(v[:, :, :KV]), dos, scale,
+                                        MASK_NONE, rows=np.arange(R), magnitudes=True)
+    g = {"dq": _f64(_at(dq, rows)), "dps": _f64(_at(dps, rows))}
+    ref = {"dq": dQ[:, :, :R], "dps": DP[:, :, :R]}
+    mag = {"dq": M["dq"][:, :, :R], "dps": M["dps"][:, :, :R]}
+    st = fa.load_library().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                  dv.data_ptr(), dps.data_ptr(), 1, 1, N + 1, d, scale,
+                                  MASK_KEY_PADDING, kv.data_ptr(), _stream())
+    assert st == fa.FA_ERR_INVALID_ARG
+    del q, k, v, do, o, lse, dq, dk, dv, dps
+    torch.cuda.empty_cache()
+    compare_grads(g, ref, mag, what, keys=("dq", "dps"))
+
+
+def test_fa_fwd_varlen_largest_total():
+    """Packed sequences filling the bound ((total + 256) H d 2 <= 2^32 - 1):
+    a short sequence, one of nearly all the rows, and another short one,
+    causal with a 64-key window; sampled rows of each sequence (its first and
+    last rows, and around byte 2^31 of the packed tensors) against the
+    oracle over the keys each row sees."""
+    import torch
+
+    import exact_attention_92_amd as fa
+    H, d, W = 1, 64, WINDOW
+    total = LIMIT // (H * d * 2) - 256
+    assert (total + 257) * H * d * 2 > LIMIT
+    lens = [300, total - 600, 300]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    what = f"fa_fwd_varlen H={H} d={d} lengths={lens} causal window {W}"
+    say(what)
+    q, k, v = (_draw((total, H, d), torch.bfloat16, s) for s in (41, 42, 43))
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((H, total), float("nan"), device="cuda")
+    cu_d = torch.from_numpy(cu).cuda()
+    scale = d ** -0.5
+    fa.fa_fwd_varlen(q, k, v, o, lse, cu_d, cu_d, max(lens), scale, MASK_CAUSAL, W)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o).any().item() and torch.isfinite(lse).all().item()
+    mid = 2 ** 31 // (H * d * 2)
+    picks = []
+    for s0, s1 in zip(cu[:-1], cu[1:]):
+        picks += [s0, s0 + 1, s0 + 64, s1 - 65, s1 - 2, s1 - 1]
+    picks += [mid - 1, mid, mid + 1]
+    rows = np.array(sorted(set(int(x) for x in picks)))
+    Os, Ls, refs = [], [], []
+    for g_row in rows:
+        s = int(np.searchsorted(cu, g_row, side="right") - 1)
+        lo = max(int(cu[s]), int(g_row) - W)
+        sl = lambda t, a, b: _f64(t[a:b].permute(1, 0, 2))[None]     # [1, H, rows, d]
+        refs.append(attention_general_ref(sl(q, g_row, g_row + 1), sl(k, lo, g_row + 1),
+                                          sl(v, lo, g_row + 1), scale, MASK_CAUSAL, W, None,
+                                          magnitudes=True))
+        Os.append(sl(o, g_row, g_row + 1))
+        Ls.append(_f64(lse[:, g_row:g_row + 1])[None])
+    ref = tuple(np.concatenate([x[i] for x in refs], axis=2) for i in range(3))
+    O, L = np.concatenate(Os, axis=2), np.concatenate(Ls, axis=2)
+    st = fa.load_library().fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                         lse.data_ptr(), cu_d.data_ptr(), cu_d.data_ptr(), 3, H,
+                                         d, total + 1, total, max(lens), scale, MASK_CAUSAL, W,
+                                         _stream())
     assert st == fa.FA_ERR_INVALID_ARG
     del q, k, v, o, lse
     torch.cuda.empty_cache()
