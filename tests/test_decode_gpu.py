@@ -148,3 +148,21 @@ def test_deterministic_and_errors_write_nothing():
     torch.cuda.synchronize()
     assert torch.isnan(o.float()).all() and torch.isnan(lse).all()
     assert fa.fa_decode_paged_workspace_bytes(2, 3, 128, 64, 10) == 2 * 3 * 2 * 130 * 4
+
+
+@pytest.mark.parametrize("B,H,bs,hi", [(65535, 2, 16, 40), (1, 65535, 8, 20)])
+def test_largest_batch_and_head_counts(B, H, bs, hi):
+    """The request and head counts at their bound (65535, a launch grid
+    dimension each), short cached lengths including 0; every output written,
+    sampled requests (the first and last included) against the oracle."""
+    what = f"decode B={B} H={H} d=64 bs={bs} lengths 0..{hi}"
+    say(what)
+    x = make_paged_decode(B, H, 64, bs, (0, hi), seed=B + H, spare=2)
+    O, L = run_decode(x, 0.125)
+    assert not np.isnan(O).any() and not np.isnan(L).any(), f"{what}: unwritten"
+    sub = np.unique(np.r_[0:3, B - 3:B, np.random.default_rng(5).integers(0, B, 60)])
+    sub = sub[(sub >= 0) & (sub < B)]
+    f = bf16_bits_to_f32
+    ref = paged_decode_ref(f(x["q"][sub]), f(x["k_pool"]), f(x["v_pool"]),
+                           x["block_tables"][sub], x["seq_lens"][sub], 0.125, magnitudes=True)
+    compare(O[sub], L[sub], ref, what)
