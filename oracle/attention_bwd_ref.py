@@ -115,8 +115,9 @@ def _head_bwd(qh, kh, vh, doh, scale, causal, n_vis, rows, row_block, mags):
             a_d = (ado * (p @ av)).sum(axis=1)            # sum_t |dO| (P |V|)
             mags["dps"][rr] = a_d
             mags["dv"][:kmax] += p.T @ ado
-            mags["dq"][rr] = scale * (ads @ ak + a_d[:, None] * (p @ ak))
-            mags["dk"][:kmax] += scale * (ads.T @ aq + p.T @ (a_d[:, None] * aq))
+            sa = abs(scale)                               # |scale * term| = |scale| |term|
+            mags["dq"][rr] = sa * (ads @ ak + a_d[:, None] * (p @ ak))
+            mags["dk"][:kmax] += sa * (ads.T @ aq + p.T @ (a_d[:, None] * aq))
     return dq, dk, dv, dps
 
 
@@ -157,8 +158,8 @@ def attention_bwd_ref(q, k, v, do, scale, mask_kind=0, kv_lens=None, heads=None,
 
         dv:  P^T |dO|
         dps: sum_t |dO_rt| (P |V|)_rt          (bounds rowsum(dO * O) too)
-        dq:  scale (|dS| |K| + dps_mag_r * P |K|)
-        dk:  scale (|dS|^T |Q| + P^T (dps_mag * |Q|))
+        dq:  |scale| (|dS| |K| + dps_mag_r * P |K|)
+        dk:  |scale| (|dS|^T |Q| + P^T (dps_mag * |Q|))
 
     The second terms carry an error of the row sum into dS = P (dP - D).
     """

@@ -220,3 +220,29 @@ def test_errors_write_nothing():
     torch.cuda.synchronize()
     for t in outs + [dps]:
         assert torch.isnan(t).all()
+
+
+BWD_EDGES = [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 383, 511, 513]
+
+
+@pytest.mark.parametrize("chunk", range(3))
+def test_random_shapes_masks_and_scales(chunk):
+    """Seeded random cases: each draws d, B, H, N (half of them at the 32-,
+    64-, 128- and 256-row block edges), the mask, the key lengths (down to 0)
+    and the scale from its own seed; dQ, dK, dV and the row sums element by
+    element against the oracle."""
+    for seed in range(900 + 10 * chunk, 900 + 10 * chunk + 10):
+        rng = np.random.default_rng(seed)
+        d = int(rng.choice([64, 128]))
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+        N = int(rng.choice(BWD_EDGES)) if rng.random() < 0.5 else int(rng.integers(1, 800))
+        mask = int(rng.integers(0, 4))
+        scale = float(d ** -0.5 * rng.choice([1.0, 1.0, -0.7, 2.5]))
+        kv_range = (0, N) if mask & MASK_KEY_PADDING else None
+        x = _raw_bwd(B, H, N, d, seed, q_mult=2.0, kv_len_range=kv_range)
+        kv = None if x["kv_lens"] is None else x["kv_lens"].tolist()
+        what = f"seed={seed} B={B} H={H} N={N} d={d} mask={mask} kv={kv} scale={scale:.4f}"
+        say(what)
+        g = run_bwd_gpu(x, scale, mask)
+        ref, mag = _oracle(x, scale, mask)
+        compare_grads(g, ref, mag, what, keys=("dq", "dk", "dv", "dps"))

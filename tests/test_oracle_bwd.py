@@ -267,20 +267,23 @@ def test_row_subsets():
         assert not np.allclose(sub[i][:, :, :44], full[i][:, :, :44])
 
 
+@pytest.mark.parametrize("scale", [0.3, -0.3])
 @pytest.mark.parametrize("mask", MASKS)
-def test_magnitudes_bound_the_values(mask):
-    """Each magnitude is a sum of |terms|, so it bounds |value| (triangle
-    inequality), and equals it when every term is non-negative; asking for
-    them changes no value."""
+def test_magnitudes_bound_the_values(mask, scale):
+    """Each magnitude is a sum of |terms|, so it is non-negative and bounds
+    |value| (triangle inequality) for either sign of the scale, and equals
+    it when every term is non-negative; asking for them changes no value."""
     q, k, v, do = _rand(2, 2, 41, 8, seed=22)
     kv = np.array([0, 30], dtype=np.int32)
-    base = attention_bwd_ref(q, k, v, do, 0.3, mask, kv)
-    *vals, mags = attention_bwd_ref(q, k, v, do, 0.3, mask, kv, magnitudes=True, row_block=9)
+    base = attention_bwd_ref(q, k, v, do, scale, mask, kv)
+    *vals, mags = attention_bwd_ref(q, k, v, do, scale, mask, kv, magnitudes=True, row_block=9)
     for i, name in enumerate(("dq", "dk", "dv", "dps")):
         assert np.max(np.abs(vals[i] - base[i])) <= 1e-12
+        finite = ~np.isnan(mags[name])
+        assert np.all(mags[name][finite] >= 0.0), name
         assert np.all(mags[name] >= np.abs(vals[i]) * (1 - 1e-12) - 1e-300), name
     # dO >= 0 and V >= 0: every term of dV and of rowsum(dO * O) is >= 0.
-    *vals, mags = attention_bwd_ref(q, k, np.abs(v), np.abs(do), 0.3, mask, kv,
+    *vals, mags = attention_bwd_ref(q, k, np.abs(v), np.abs(do), scale, mask, kv,
                                     magnitudes=True)
     assert np.max(np.abs(mags["dv"] - vals[2])) <= 1e-12
     assert np.max(np.abs(mags["dps"] - vals[3])) <= 1e-12
