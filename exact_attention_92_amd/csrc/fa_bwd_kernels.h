@@ -62,6 +62,7 @@ struct BwdParams {
   float ascale;          // |gscale|, applied to dK (Q is staged sign-flipped)
   unsigned qsign;        // bf16 sign flip applied to Q when scale < 0
   int causal;
+  int hg;                // heads map_work visits together (head_group)
 };
 
 // Enqueues the d = 64 dQ and dK/dV kernels (defined in fa_bwd_d64.hip);
@@ -135,7 +136,7 @@ void fa_bwd_dq_kernel(BwdParams p) {
   const int N = p.N;
 
   int bh, qb;
-  map_work(p.nb, causal, bh, qb);
+  map_work(p.nb, causal, p.hg, bh, qb);
   const int b = bh / p.H;
   const size_t hoff = (size_t)bh * (size_t)N * D;
   const uint16_t* Kh = (const uint16_t*)p.k + hoff;
@@ -431,7 +432,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   const int N = p.N;
 
   int bh, kb;
-  map_work(p.nb, false, bh, kb);   // causal: key block 0 (the most query blocks) first
+  map_work(p.nb, false, p.hg, bh, kb);   // causal: key block 0 (the most query blocks) first
   const int b = bh / p.H;
   const size_t hoff = (size_t)bh * (size_t)N * D;
   const int n_vis = visible_len(p, b);
@@ -567,19 +568,28 @@ constexpr long long kCUs = 256;   // compute units of an MI355X
 // twice over for causal masks (once otherwise), else 128 rows (4 waves);
 // then dK and dV: 128 keys per workgroup.  Both on stream s, in that order;
 // false if a launch failed (the dK/dV kernel is then not enqueued).
+template <int D, int NW>
+void launch_dq(unsigned grid, hipStream_t s, BwdParams p) {
+  static std::atomic<long long> resident{0};
+  p.hg = head_group(fa_bwd_dq_kernel<D, NW>, 64 * NW, p.causal != 0, grid, resident);
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<D, NW>), dim3(grid), dim3(64 * NW), 0, s, p);
+}
+
 template <int D>
 bool launch_bwd(BwdParams p, int B, hipStream_t s) {
   const long long grid256 = (long long)B * p.H * ((p.N + 255) / 256);
   const bool big = grid256 >= (p.causal ? 2 : 1) * kCUs;
   const int BM = big ? 256 : 128;
   p.nb = (p.N + BM - 1) / BM;
-  const dim3 gq((unsigned)(B * p.H * p.nb)), bq(big ? 512 : 256);
-  if (big) hipLaunchKernelGGL((fa_bwd_dq_kernel<D, 8>), gq, bq, 0, s, p);
-  else hipLaunchKernelGGL((fa_bwd_dq_kernel<D, 4>), gq, bq, 0, s, p);
+  const unsigned gq = (unsigned)(B * p.H * p.nb);
+  if (big) launch_dq<D, 8>(gq, s, p);
+  else launch_dq<D, 4>(gq, s, p);
   if (hipGetLastError() != hipSuccess) return false;
   p.nb = (p.N + 32 * kKvWaves - 1) / (32 * kKvWaves);
-  const dim3 gk((unsigned)(B * p.H * p.nb)), bk(64 * kKvWaves);
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D>), gk, bk, 0, s, p);
+  const unsigned gk = (unsigned)(B * p.H * p.nb);
+  static std::atomic<long long> resident_kv{0};
+  p.hg = head_group(fa_bwd_dkdv_kernel<D>, 64 * kKvWaves, p.causal != 0, gk, resident_kv);
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D>), dim3(gk), dim3(64 * kKvWaves), 0, s, p);
   return hipGetLastError() == hipSuccess;
 }
 

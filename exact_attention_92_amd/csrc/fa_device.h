@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace fa92 {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -91,19 +93,16 @@ __device__ __forceinline__ void transpose4x8(const u32x4_t (&x)[4], u32x2_t (&ou
 // heads split evenly XCD x owns the heads bh = x, x + 8, x + 16, ... (each
 // head's tensors stay in one XCD's L2, and every XCD gets heads of every
 // batch entry, so per-batch key lengths balance across XCDs) and visits
-// their blocks rank by rank, FA_WORK_GROUP (four) heads at a time; rank 0 is
-// block nb-1 when heavy_last, else block 0.  Otherwise XCD x gets the
+// their blocks rank by rank, hg heads at a time (head_group below); rank 0
+// is block nb-1 when heavy_last, else block 0.  Otherwise XCD x gets the
 // contiguous logical range [x*G/8, (x+1)*G/8).
-#ifndef FA_WORK_GROUP
-#define FA_WORK_GROUP 4
-#endif
-__device__ __forceinline__ void map_work(int nb, bool heavy_last, int& bh, int& blk) {
+__device__ __forceinline__ void map_work(int nb, bool heavy_last, int hg, int& bh, int& blk) {
   const int G = gridDim.x;
   const int w = blockIdx.x;
   const int BH = G / nb;
   if (G % 8 == 0 && BH % 8 == 0) {
     const int hx = BH / 8, i = w / 8;
-    const int g = (hx % FA_WORK_GROUP == 0) ? FA_WORK_GROUP : hx;
+    const int g = (hx % hg == 0) ? hg : hx;
     const int grp = i / (g * nb), j = i - grp * (g * nb);
     bh = (grp * g + j % g) * 8 + (w % 8);
     const int r = j / g;
@@ -114,6 +113,32 @@ __device__ __forceinline__ void map_work(int nb, bool heavy_last, int& bh, int& 
   bh = L / nb;
   const int r = L - bh * nb;
   blk = heavy_last ? (nb - 1 - r) : r;
+}
+
+// Heads per map_work group, chosen on the host: 8 for causal launches whose
+// workgroups are all resident at once -- each CU then holds workgroups a
+// fixed distance apart in its XCD's order, and a rank-major run over 8 heads
+// puts a heavy causal rank and a light one there where a run over 4 pairs
+// equal ranks -- else 4, which keeps the L2 working set smaller.  `resident`
+// caches the kernel's resident-workgroup count once an occupancy query has
+// succeeded (until then 4 is used).
+template <typename Kernel>
+inline int head_group(Kernel kernel, int threads, bool causal, long long grid,
+                      std::atomic<long long>& resident) {
+  if (!causal) return 4;
+  long long res = resident.load(std::memory_order_relaxed);
+  if (res <= 0) {
+    int occ = 0, dev = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, threads, 0) == hipSuccess &&
+        occ > 0 && hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        cus > 0) {
+      res = (long long)occ * cus;
+      resident.store(res, std::memory_order_relaxed);
+    }
+    (void)hipGetLastError();   // a failed query is not the caller's error
+  }
+  return (res > 0 && grid <= res) ? 8 : 4;
 }
 
 }  // namespace fa92

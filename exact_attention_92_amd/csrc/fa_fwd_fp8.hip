@@ -101,6 +101,7 @@ struct P8Params {
   float ascale;     // |scale|, at least 1e-30
   unsigned qsign;   // E4M3 sign flip applied to Q when scale < 0
   int causal;
+  int hg;           // heads map_work visits together (head_group)
 };
 
 template <int D, int NW>
@@ -135,7 +136,7 @@ void fa_fwd_fp8_kernel(P8Params p) {
   const int N = p.N;
 
   int bh, qb;
-  map_work(p.nqb, causal, bh, qb);
+  map_work(p.nqb, causal, p.hg, bh, qb);
   const int b = bh / p.H;
   const size_t hoff = (size_t)bh * (size_t)N * D;
   const uint8_t* Kh = (const uint8_t*)p.k + hoff;
@@ -333,6 +334,13 @@ void fa_fwd_fp8_kernel(P8Params p) {
 
 constexpr long long kCUs = 256;   // compute units of an MI355X
 
+template <int D, int NW>
+void launch_fp8(unsigned grid, hipStream_t s, P8Params p) {
+  static std::atomic<long long> resident{0};
+  p.hg = head_group(fa_fwd_fp8_kernel<D, NW>, 64 * NW, p.causal != 0, grid, resident);
+  hipLaunchKernelGGL((fa_fwd_fp8_kernel<D, NW>), dim3(grid), dim3(64 * NW), 0, s, p);
+}
+
 }  // namespace
 
 extern "C" int fa_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale,
@@ -374,13 +382,13 @@ extern "C" int fa_fwd_fp8(const void* q, const void* k, const void* v, const flo
   p.qsign = (signbit(scale) && scale != 0.f) ? 0x80808080u : 0u;
   p.causal = causal ? 1 : 0;
   hipStream_t s = (hipStream_t)stream;
-  const dim3 grid((unsigned)(B * H * p.nqb)), block(big ? 512 : 256);
+  const unsigned grid = (unsigned)(B * H * p.nqb);
   if (d == 128) {
-    if (big) hipLaunchKernelGGL((fa_fwd_fp8_kernel<128, 8>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((fa_fwd_fp8_kernel<128, 4>), grid, block, 0, s, p);
+    if (big) launch_fp8<128, 8>(grid, s, p);
+    else launch_fp8<128, 4>(grid, s, p);
   } else {
-    if (big) hipLaunchKernelGGL((fa_fwd_fp8_kernel<64, 8>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((fa_fwd_fp8_kernel<64, 4>), grid, block, 0, s, p);
+    if (big) launch_fp8<64, 8>(grid, s, p);
+    else launch_fp8<64, 4>(grid, s, p);
   }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

@@ -48,9 +48,9 @@
  *
  * Ownership and side effects: the caller owns every buffer; the library
  * allocates no memory.  Its only state is a process-wide cache of how many
- * workgroups of each forward kernel the device holds at once (the first
- * occupancy query that succeeds; it sets the grid size and the order of
- * the work only).  It writes o and lse and nothing else.  Inputs are only
+ * workgroups of each kernel the device holds at once (the first occupancy
+ * query that succeeds; it sets the grid size and the order of the work
+ * only).  It writes o and lse and nothing else.  Inputs are only
  * read.
  *
  * Errors: every argument is checked on the host before anything is
