@@ -114,6 +114,19 @@ def _check(nm, t, dtype, shape=None, device=None, contiguous=True):
         raise ValueError(f"{nm} must be {list(shape)}, got {list(t.shape)}")
 
 
+def _overlapping(t):
+    """True if two index tuples of t address the same element: with its
+    dimensions ordered by stride, each stride must be at least the span of
+    the dimensions below it (dimensions of size 1 impose nothing)."""
+    dims = sorted((st, n) for st, n in zip(t.stride(), t.shape) if n > 1)
+    span = 1
+    for st, n in dims:
+        if st < span:
+            return True
+        span = st * (n - 1) + span
+    return False
+
+
 def _check_kv_lens(kv_lens, B, device):
     import torch
     if kv_lens is not None:
@@ -175,6 +188,8 @@ def fa_fwd_general(q, k, v, o, lse, scale, mask_kind=FA_MASK_NONE, window_left=-
         _check(nm, t, torch.bfloat16, (B, H, rows, d), q.device, contiguous=False)
         if t.stride(3) != 1:
             raise ValueError(f"{nm} must have a contiguous last dimension")
+        if nm == "o" and _overlapping(t):
+            raise ValueError("o must not be an overlapping view (every element written once)")
         strides.append((ctypes.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2)))
     _check("lse", lse, torch.float32, (B, H, Nq), q.device)
     _check_kv_lens(kv_lens, B, q.device)

@@ -562,8 +562,6 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   }
 }
 
-constexpr long long kCUs = 256;   // compute units of an MI355X
-
 // dQ and D: 256-row workgroups (8 waves) when they fill the chip at least
 // twice over for causal masks (once otherwise), else 128 rows (4 waves);
 // then dK and dV: 128 keys per workgroup.  Both on stream s, in that order;
@@ -571,7 +569,8 @@ constexpr long long kCUs = 256;   // compute units of an MI355X
 template <int D, int NW>
 void launch_dq(unsigned grid, hipStream_t s, BwdParams p) {
   static std::atomic<long long> resident{0};
-  p.hg = head_group(fa_bwd_dq_kernel<D, NW>, 64 * NW, p.causal != 0, grid, resident);
+  p.hg = head_group(p.causal != 0, grid,
+                    resident_workgroups(fa_bwd_dq_kernel<D, NW>, 64 * NW, resident));
   hipLaunchKernelGGL((fa_bwd_dq_kernel<D, NW>), dim3(grid), dim3(64 * NW), 0, s, p);
 }
 
@@ -588,7 +587,8 @@ bool launch_bwd(BwdParams p, int B, hipStream_t s) {
   p.nb = (p.N + 32 * kKvWaves - 1) / (32 * kKvWaves);
   const unsigned gk = (unsigned)(B * p.H * p.nb);
   static std::atomic<long long> resident_kv{0};
-  p.hg = head_group(fa_bwd_dkdv_kernel<D>, 64 * kKvWaves, p.causal != 0, gk, resident_kv);
+  p.hg = head_group(p.causal != 0, gk,
+                    resident_workgroups(fa_bwd_dkdv_kernel<D>, 64 * kKvWaves, resident_kv));
   hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D>), dim3(gk), dim3(64 * kKvWaves), 0, s, p);
   return hipGetLastError() == hipSuccess;
 }

@@ -41,6 +41,12 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// max(lane l's value, lane (l ^ 32)'s value).
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Two floats -> packed bf16 pair (round to nearest even).
 __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
   f32x2_t v = {lo, hi};
@@ -51,6 +57,11 @@ __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
 __device__ __forceinline__ float dot_bf16x2(unsigned a, unsigned b, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
+// acc + (lo + hi) of a packed bf16 pair, in fp32.
+__device__ __forceinline__ float sum_bf16x2(unsigned pair, float acc) {
+  return dot_bf16x2(pair, 0x3f803f80u, acc);
 }
 
 // Raw buffer resource over [base, base + bytes): loads past the end return 0.
@@ -89,17 +100,25 @@ __device__ __forceinline__ void transpose4x8(const u32x4_t (&x)[4], u32x2_t (&ou
 }
 
 // Workgroups are dispatched round-robin over the 8 XCDs (w % 8), in order
-// within one.  Maps the linear workgroup id to (head, block) so that when the
-// heads split evenly XCD x owns the heads bh = x, x + 8, x + 16, ... (each
-// head's tensors stay in one XCD's L2, and every XCD gets heads of every
-// batch entry, so per-batch key lengths balance across XCDs) and visits
-// their blocks rank by rank, hg heads at a time (head_group below); rank 0
-// is block nb-1 when heavy_last, else block 0.  Otherwise XCD x gets the
-// contiguous logical range [x*G/8, (x+1)*G/8).
-__device__ __forceinline__ void map_work(int nb, bool heavy_last, int hg, int& bh, int& blk) {
-  const int G = gridDim.x;
-  const int w = blockIdx.x;
+// within one.  Maps work item w of G (nb blocks for each of G / nb heads) to
+// (head bh, block blk).  When the heads split evenly, XCD x owns the heads
+// bh = x, x + 8, x + 16, ... (each head's tensors stay in one XCD's L2, and
+// every XCD gets heads of every batch entry, so per-batch key lengths
+// balance across XCDs) and visits their blocks rank by rank, hg heads at a
+// time (head_group below); rank 0 is block nb-1 when heavy_last (causal
+// query blocks: heaviest first), else block 0.  Otherwise XCD x gets the
+// contiguous logical range [x*G/8, (x+1)*G/8).  With spread (packed
+// sequences of unequal lengths, where binding heads to XCDs would bind
+// whole sequences to them) the order is rank-major over all heads.
+__device__ __forceinline__ void map_work(int nb, bool heavy_last, int hg, bool spread, int w,
+                                         int G, int& bh, int& blk) {
   const int BH = G / nb;
+  if (spread) {
+    bh = w % BH;
+    const int r = w / BH;
+    blk = heavy_last ? (nb - 1 - r) : r;
+    return;
+  }
   if (G % 8 == 0 && BH % 8 == 0) {
     const int hx = BH / 8, i = w / 8;
     const int g = (hx % hg == 0) ? hg : hx;
@@ -115,30 +134,42 @@ __device__ __forceinline__ void map_work(int nb, bool heavy_last, int hg, int& b
   blk = heavy_last ? (nb - 1 - r) : r;
 }
 
-// Heads per map_work group, chosen on the host: 8 for causal launches whose
-// workgroups are all resident at once -- each CU then holds workgroups a
+// The same for a launch with one workgroup per work item.
+__device__ __forceinline__ void map_work(int nb, bool heavy_last, int hg, int& bh, int& blk) {
+  map_work(nb, heavy_last, hg, false, (int)blockIdx.x, (int)gridDim.x, bh, blk);
+}
+
+// Compute units of an MI355X: the grid size of a looping launch while the
+// runtime cannot say how many workgroups the chip holds.
+constexpr long long kCUs = 256;
+
+// Workgroups of `kernel` the device holds at once (occupancy per compute
+// unit x compute units), cached in `cache` once a query succeeds; 0 while
+// the runtime cannot answer (nothing is cached then, and the failed query
+// is not left as the caller's error).
+template <typename Kernel>
+inline long long resident_workgroups(Kernel kernel, int threads, std::atomic<long long>& cache) {
+  const long long known = cache.load(std::memory_order_relaxed);
+  if (known > 0) return known;
+  int occ = 0, dev = 0, cus = 0;
+  const bool ok =
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, threads, 0) == hipSuccess &&
+      occ > 0 && hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      cus > 0;
+  (void)hipGetLastError();
+  if (!ok) return 0;
+  cache.store((long long)occ * cus, std::memory_order_relaxed);
+  return (long long)occ * cus;
+}
+
+// Heads per map_work group: 8 for causal launches whose work items are all
+// resident at once (known resident count) -- each CU then holds items a
 // fixed distance apart in its XCD's order, and a rank-major run over 8 heads
 // puts a heavy causal rank and a light one there where a run over 4 pairs
-// equal ranks -- else 4, which keeps the L2 working set smaller.  `resident`
-// caches the kernel's resident-workgroup count once an occupancy query has
-// succeeded (until then 4 is used).
-template <typename Kernel>
-inline int head_group(Kernel kernel, int threads, bool causal, long long grid,
-                      std::atomic<long long>& resident) {
-  if (!causal) return 4;
-  long long res = resident.load(std::memory_order_relaxed);
-  if (res <= 0) {
-    int occ = 0, dev = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, threads, 0) == hipSuccess &&
-        occ > 0 && hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        cus > 0) {
-      res = (long long)occ * cus;
-      resident.store(res, std::memory_order_relaxed);
-    }
-    (void)hipGetLastError();   // a failed query is not the caller's error
-  }
-  return (res > 0 && grid <= res) ? 8 : 4;
+// equal ranks -- else 4, which keeps the L2 working set smaller.
+inline int head_group(bool causal, long long items, long long resident) {
+  return (causal && resident > 0 && items <= resident) ? 8 : 4;
 }
 
 }  // namespace fa92

@@ -70,71 +70,25 @@
 #include <atomic>
 
 #include "fa_api.h"
+#include "fa_device.h"
 
 namespace {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+using namespace fa92;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kOverflowSum = 1048576.f;  // 2^20: largest block row sum kept on the fast path
 constexpr float kTau = 8.0f;         // fp32 kernel: max-move threshold, log2 units
-constexpr float kMinScale = 1e-30f;
-
-__device__ __forceinline__ f32x16_t mfma_bf16(u32x4_t a, u32x4_t b, f32x16_t c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
 
 __device__ __forceinline__ f32x16_t mfma_f32(float a, float b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-// Value of lane (l ^ 32) combined with lane l's own value.
-__device__ __forceinline__ float pair_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
-  f32x2_t v = {lo, hi};
-  return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2_t));
-}
-
-// acc + (lo + hi) of a packed bf16 pair, in fp32 (v_dot2c_f32_bf16 with 1.0).
-__device__ __forceinline__ float sum_bf16x2(unsigned pair, float acc) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pair),
-                                         __builtin_bit_cast(bf16x2_t, 0x3f803f80u), acc, false);
-}
-
-// Raw buffer resource over [base, base + bytes): loads past the end return 0.
-// Word 3 selects the raw 32-bit data format used by CDNA buffer loads.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
-__device__ __forceinline__ u32x4_t buf_load16(rsrc_t r, uint32_t voff) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
-}
-
-// Row of K that MFMA row m reads: bits 2 and 3 of m swapped.  With it, the
-// accumulator register r of lane-half h holds key 16*(r/8) + 8*h + (r%8) of
-// each 32-key tile, so 8 consecutive registers are 8 consecutive keys.
-__device__ __forceinline__ int k_row_perm(int m) {
-  return (m & 0x13) | ((m & 4) << 1) | ((m & 8) >> 1);
-}
+// Row of K that MFMA row m reads (row_perm): with it, the accumulator
+// register r of lane-half h holds key 16*(r/8) + 8*h + (r%8) of each 32-key
+// tile, so 8 consecutive registers are 8 consecutive keys.
+__device__ __forceinline__ int k_row_perm(int m) { return row_perm(m); }
 
 // Scheduling hint for a run of NM MFMAs, each fed by one LDS operand read:
 // issue AHEAD reads first, then alternate MFMA and read.  LDS round trips
@@ -152,61 +106,11 @@ __device__ __forceinline__ void mfma_read_ahead() {
   }
 }
 
-// Heads whose query blocks an XCD visits together (rank-major within the
-// group), chosen on the host: 4, which keeps the L2 working set small; 8 for
-// causal launches whose workgroups are all resident at once.  There each CU
-// takes workgroups that lie a fixed distance apart in its XCD's order, and a
-// rank-major run over 8 heads puts a heavy causal rank and a light one on the
-// same CU where a run over 4 pairs equal ranks (measured +28% at B = 4,
-// H = 16, N = 1024, d = 64; on grids larger than the chip 8 heads gave the
-// same speed with 1.4x the HBM traffic).
-#ifndef FA_HEAD_GROUP
-#define FA_HEAD_GROUP 4
-#endif
-#ifndef FA_HEAD_GROUP_ONE_WAVE
-#define FA_HEAD_GROUP_ONE_WAVE 8
-#endif
-// Maps the linear workgroup id to (head, query block).  Workgroups are
-// dispatched round-robin over the 8 XCDs (w % 8), and in order within one.
-// When the heads split evenly, XCD x owns the heads bh = x, x + 8, x + 16, ...
-// (each head's K/V stays in one XCD's L2; striding rather than a contiguous
-// range gives every XCD heads of every batch entry, so per-batch key
-// lengths do not load one XCD more than another) and visits their query
-// blocks rank by rank: for causal masks the last (heaviest) query block of
-// every head first, so the light ones fill the tail.  Otherwise XCD x gets
-// the contiguous logical range [x*G/8, (x+1)*G/8), heavy query blocks first
-// within each head.
-//
-// With spread (packed sequences of unequal lengths, where binding heads to
-// XCDs would bind whole sequences to them), the order is rank-major over all
-// (batch, head): consecutive workgroups, and so the XCDs, take every
-// sequence's blocks of one rank before the next rank.
-__device__ __forceinline__ void map_block(int nqb, bool causal, int& bh, int& qb,
-                                          bool spread, int w, int G, int hg) {
-  const int BH = G / nqb;
-  if (spread) {
-    bh = w % BH;
-    const int r = w / BH;
-    qb = causal ? (nqb - 1 - r) : r;
-    return;
-  }
-  if (G % 8 == 0 && BH % 8 == 0) {
-    // XCD x = w % 8 owns heads x + 8t, t < BH/8; it visits their query
-    // blocks rank by rank (heaviest causal rank first), head by head.
-    const int hx = BH / 8, i = w / 8;
-    const int g = (hx % hg == 0) ? hg : hx;   // heads visited together
-    const int grp = i / (g * nqb), j = i - grp * (g * nqb);
-    bh = (grp * g + j % g) * 8 + (w % 8);
-    const int r = j / g;
-    qb = causal ? (nqb - 1 - r) : r;
-    return;
-  }
-  const int L = (G % 8 == 0) ? (w % 8) * (G / 8) + w / 8 : w;
-  bh = L / nqb;
-  const int r = L - bh * nqb;
-  qb = causal ? (nqb - 1 - r) : r;
-}
-
+// Heads an XCD visits together for launches whose items are not all
+// resident (head_group in fa_device.h chooses 8 for causal launches that fit
+// the chip at once: measured +19-23% at B = 4, H = 16, N = 1024, d = 64/128;
+// on grids larger than the chip 8 heads gave the same speed with 1.4x the
+// HBM traffic).
 struct Params {
   const void* q;
   const void* k;
@@ -216,7 +120,7 @@ struct Params {
   const int32_t* kv_lens;
   int H, N, nqb;    // N: query rows (and keys, unless the general layout is used)
   int items;        // work items (head, query block) = B * H * nqb
-  int hg;           // heads an XCD visits together (see map_block), >= 1
+  int hg;           // heads an XCD visits together (map_work), 4 or 8
   float c;          // |scale| * log2(e), >= kMinScale * log2(e)
   unsigned qsign;   // sign flip applied to Q when scale < 0
   int causal;
@@ -302,7 +206,7 @@ void fa_fwd_bf16_kernel(Params p) {
     int N = p.N;
 
     int bh, qb;
-    map_block(p.nqb, causal, bh, qb, VL, w_item, p.items, p.hg);
+    map_work(p.nqb, causal, p.hg, VL, w_item, p.items, bh, qb);
     const int b = bh / p.H;
     int Nk = GEN ? p.Nk : N;
     int off = GEN ? p.off : 0;                // key position of query row 0
@@ -606,7 +510,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_f32_kernel(Params p) {
   const int N = p.N;
 
   int bh, qb;
-  map_block(p.nqb, causal, bh, qb, false, blockIdx.x, gridDim.x, p.hg);
+  map_work(p.nqb, causal, p.hg, bh, qb);
   const int b = bh / p.H;
   const size_t hoff = (size_t)bh * (size_t)N * D;
   const float* __restrict__ Qh = (const float*)p.q + hoff;
@@ -731,7 +635,7 @@ bool bf16_head_dim(int d) { return d == 32 || d == 64 || d == 96 || d == 128 || 
 
 int check_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
                int B, int H, int N, int d, float scale, int mask_kind, const int32_t* kv_lens,
-               int bm, bool bf16) {
+               int bm, int pad_rows, bool bf16) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   const uintptr_t al = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse;
   if (al & 15u) return FA_ERR_INVALID_ARG;
@@ -742,9 +646,9 @@ int check_args(const void* q, const void* k, const void* v, const void* o, const
   if (bf16 ? !bf16_head_dim(d) : (d != 64 && d != 128)) return FA_ERR_UNSUPPORTED;
   const long long nqb = ((long long)N + bm - 1) / bm;
   if ((long long)B * H * nqb > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
-  // One head's rows (plus one block of rows past the end) are addressed with
-  // 32-bit byte offsets.
-  if (((long long)N + bm) * d * 4 > 0xffffffffLL) return FA_ERR_INVALID_ARG;
+  // One head's rows (plus pad_rows past the end) are addressed with 32-bit
+  // byte offsets.
+  if (((long long)N + pad_rows) * d * 4 > 0xffffffffLL) return FA_ERR_INVALID_ARG;
   return FA_OK;
 }
 
@@ -765,46 +669,22 @@ Params make_params(const void* q, const void* k, const void* v, void* o, float* 
   p.c = a * kLog2e;
   p.qsign = signbit(scale) && scale != 0.f ? 0x80008000u : 0u;
   p.causal = (mask_kind & FA_MASK_CAUSAL) ? 1 : 0;
-  p.hg = FA_HEAD_GROUP;
+  p.hg = 4;
   return p;
 }
 
-constexpr long long kCUs = 256;   // compute units of an MI355X
-
-// One bf16 forward launch: 8-wave (256-row) workgroups when big, else 4-wave.
-// Workgroups of one kernel instantiation that the chip holds at once
-// (occupancy per compute unit x compute units).  The first successful query
-// is cached; while the runtime cannot answer (it only sets the grid size),
-// one workgroup per compute unit is assumed and nothing is cached.
-template <int D, int NW, int MODE>
-long long resident_workgroups() {
-  static std::atomic<long long> cached{0};
-  const long long known = cached.load(std::memory_order_relaxed);
-  if (known > 0) return known;
-  int occ = 0, dev = 0, cus = 0;
-  const bool ok =
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fa_fwd_bf16_kernel<D, NW, MODE>,
-                                                   64 * NW, 0) == hipSuccess &&
-      occ > 0 && hipGetDevice(&dev) == hipSuccess &&
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-      cus > 0;
-  (void)hipGetLastError();   // a failed query is not the caller's error
-  if (!ok) return kCUs;
-  cached.store((long long)occ * cus, std::memory_order_relaxed);
-  return (long long)occ * cus;
-}
-
-// One launch over p.items work items.  Contiguous self-attention with
-// d <= 128 launches at most as many workgroups as the chip holds at once and
-// lets each loop over its items (no workgroup start per item; the snake order
-// of the kernel balances the causal ranks); the other layouts and d = 256
-// launch one workgroup per item.
+// One bf16 forward launch over p.items work items.  Contiguous
+// self-attention with d <= 128 launches at most as many workgroups as the
+// chip holds at once and lets each loop over its items (no workgroup start
+// per item; the snake order of the kernel balances the causal ranks); the
+// other layouts and d = 256 launch one workgroup per item.
 template <int D, int NW, int MODE>
 void launch_one(hipStream_t s, Params p) {
-  const long long resident = resident_workgroups<D, NW, MODE>();
-  if (p.causal && p.items <= resident) p.hg = FA_HEAD_GROUP_ONE_WAVE;
-  const long long grid =
-      (MODE == 0 && D <= 128) ? std::min<long long>(p.items, resident) : p.items;
+  static std::atomic<long long> cache{0};
+  const long long resident = resident_workgroups(fa_fwd_bf16_kernel<D, NW, MODE>, 64 * NW, cache);
+  p.hg = head_group(p.causal != 0, p.items, resident);
+  const long long cap = resident > 0 ? resident : kCUs;
+  const long long grid = (MODE == 0 && D <= 128) ? std::min<long long>(p.items, cap) : p.items;
   hipLaunchKernelGGL((fa_fwd_bf16_kernel<D, NW, MODE>), dim3((unsigned)grid), dim3(64 * NW), 0,
                      s, p);
 }
@@ -832,7 +712,10 @@ void launch_bf16(int d, bool big, hipStream_t s, const Params& p) {
 extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                       int H, int N, int d, float scale, int mask_kind, const int32_t* kv_lens,
                       void* stream) {
-  const int st = check_args(q, k, v, o, lse, B, H, N, d, scale, mask_kind, kv_lens, 256, true);
+  // Work items are 128- or 256-row query blocks: B * H * ceil(N / 128)
+  // bounds both grids.
+  const int st =
+      check_args(q, k, v, o, lse, B, H, N, d, scale, mask_kind, kv_lens, 128, 256, true);
   if (st != FA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   // 256-row workgroups (8 waves, one per CU) share each K/V tile among more
@@ -945,7 +828,7 @@ extern "C" int fa_fwd_f32(const void* q, const void* k, const void* v, void* o, 
                           int H, int N, int d, float scale, int mask_kind, const int32_t* kv_lens,
                           void* stream) {
   constexpr int BM = 32 * kWaves;
-  const int st = check_args(q, k, v, o, lse, B, H, N, d, scale, mask_kind, kv_lens, BM, false);
+  const int st = check_args(q, k, v, o, lse, B, H, N, d, scale, mask_kind, kv_lens, BM, BM, false);
   if (st != FA_OK) return st;
   const int nqb = (N + BM - 1) / BM;
   const Params p = make_params(q, k, v, o, lse, H, N, nqb, scale, mask_kind, kv_lens);

@@ -66,11 +66,6 @@ __device__ __forceinline__ i32x8_t join(u32x4_t lo, u32x4_t hi) {
                  (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
 
-__device__ __forceinline__ float pair_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
 // Four floats (already scaled into [0, 448]) -> four E4M3 bytes, nearest even.
 __device__ __forceinline__ unsigned pack_fp8x4(float a, float b, float c, float d) {
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
@@ -332,12 +327,11 @@ void fa_fwd_fp8_kernel(P8Params p) {
   }
 }
 
-constexpr long long kCUs = 256;   // compute units of an MI355X
-
 template <int D, int NW>
 void launch_fp8(unsigned grid, hipStream_t s, P8Params p) {
   static std::atomic<long long> resident{0};
-  p.hg = head_group(fa_fwd_fp8_kernel<D, NW>, 64 * NW, p.causal != 0, grid, resident);
+  p.hg = head_group(p.causal != 0, grid,
+                    resident_workgroups(fa_fwd_fp8_kernel<D, NW>, 64 * NW, resident));
   hipLaunchKernelGGL((fa_fwd_fp8_kernel<D, NW>), dim3(grid), dim3(64 * NW), 0, s, p);
 }
 

@@ -66,3 +66,17 @@ def test_check_names_the_problem():
         fa._check("lse", torch.zeros(3, dtype=torch.float64), torch.float32)
     with pytest.raises(TypeError, match="kv_lens"):
         fa._check("kv_lens", [1, 2], torch.int32)
+
+
+def test_overlapping_view_detection():
+    """The stride rule that keeps overlapping output views away from the
+    general forward: dense and permuted layouts pass, expanded or aliasing
+    views do not, strided views with gaps pass."""
+    x = torch.empty(2, 3, 10, 8)
+    assert not fa._overlapping(x)
+    assert not fa._overlapping(x.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3))
+    assert not fa._overlapping(x[:, :, ::2])
+    assert not fa._overlapping(torch.empty(1, 3, 10, 8))
+    assert fa._overlapping(torch.empty(1, 3, 10, 8).expand(2, 3, 10, 8))
+    assert fa._overlapping(torch.empty(2, 10, 8).unsqueeze(1).expand(2, 3, 10, 8))
+    assert fa._overlapping(torch.empty(2, 3, 80).as_strided((2, 3, 10, 8), (240, 80, 4, 1)))

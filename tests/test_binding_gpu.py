@@ -36,6 +36,10 @@ def test_one_bad_tensor_is_refused_and_nothing_is_written():
         "fa_fwd_general host lse": lambda: fa.fa_fwd_general(q, q, q, o, lse.cpu(), 0.1),
         "fa_fwd_general host kv_lens": lambda: fa.fa_fwd_general(q, q, q, o, lse, 0.1, 2, -1,
                                                                  kv.cpu()),
+        "fa_fwd_general overlapping o": lambda: fa.fa_fwd_general(
+            q, q, q, _nan((1, H, N, d), torch.bfloat16).expand(B, H, N, d), lse, 0.1),
+        "fa_fwd_general o rows aliasing heads": lambda: fa.fa_fwd_general(
+            q, q, q, _nan((B, N, d), torch.bfloat16).unsqueeze(1).expand(B, H, N, d), lse, 0.1),
         "fa_bwd strided dq": lambda: fa.fa_bwd(
             q, q, q, q, lse, q, _nan((B, H, N, 2 * d), torch.bfloat16)[..., ::2],
             o, o.clone(), lse.clone(), 0.1),
