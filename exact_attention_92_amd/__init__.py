@@ -40,10 +40,13 @@ FA_OK = 0
 FA_ERR_INVALID_ARG = -1
 FA_ERR_UNSUPPORTED = -2
 FA_ERR_HIP = -3
+FA_ERR_SCRATCH = -4
+DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa92.so")
 EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_general", "fa_fwd_varlen", "fa_fwd_fp8", "fa_bwd",
-           "fa_decode_paged", "fa_decode_paged_workspace_bytes", "fa_strerror")
+           "fa_decode_paged", "fa_decode_paged_noalloc", "fa_decode_paged_workspace_bytes",
+           "fa_strerror")
 
 _lib = None
 
@@ -78,6 +81,8 @@ def load_library():
     lib.fa_fwd_fp8.restype = i32
     lib.fa_decode_paged.argtypes = [vp] * 8 + [i32] * 6 + [f32, vp]
     lib.fa_decode_paged.restype = i32
+    lib.fa_decode_paged_noalloc.argtypes = [vp] * 7 + [i32] * 6 + [f32, vp]
+    lib.fa_decode_paged_noalloc.restype = i32
     lib.fa_decode_paged_workspace_bytes.argtypes = [i32] * 5
     lib.fa_decode_paged_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_bwd.argtypes = [vp] * 10 + [i32, i32, i32, i32, f32, i32, vp, vp]
@@ -271,6 +276,20 @@ def fa_decode_paged(q, k_pool, v_pool, block_tables, seq_lens, o, lse, workspace
     seq_lens int32 [B]; writes o (bf16 [B, H, d]) and lse (float32 [B, H])."""
     import torch
     lib = load_library()
+    B, H, d, nblk, bs = _check_decode(q, k_pool, v_pool, block_tables, seq_lens, o, lse)
+    need = fa_decode_paged_workspace_bytes(B, H, d, bs, block_tables.shape[1])
+    _check("workspace", workspace, torch.float32, device=q.device)
+    if workspace.numel() * 4 < need:
+        raise ValueError(f"workspace must hold >= {need} bytes")
+    st = lib.fa_decode_paged(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+                             _ptr(seq_lens), _ptr(o), _ptr(lse), _ptr(workspace), B, H, d, bs,
+                             block_tables.shape[1], nblk, float(scale),
+                             ctypes.c_void_p(_stream_handle(stream, q.device)))
+    if st != FA_OK:
+        raise FaError(st, fa_strerror(st))
+
+def _check_decode(q, k_pool, v_pool, block_tables, seq_lens, o, lse):
+    import torch
     _check("q", q, torch.bfloat16)
     _check("k_pool", k_pool, torch.bfloat16, device=q.device)
     if q.dim() != 3 or k_pool.dim() != 4:
@@ -286,17 +305,22 @@ def fa_decode_paged(q, k_pool, v_pool, block_tables, seq_lens, o, lse, workspace
         raise ValueError("block_tables must be [B, max_blocks]")
     _check("seq_lens", seq_lens, torch.int32, (B,), q.device)
     _check("lse", lse, torch.float32, (B, H), q.device)
-    need = fa_decode_paged_workspace_bytes(B, H, d, bs, block_tables.shape[1])
-    _check("workspace", workspace, torch.float32, device=q.device)
-    if workspace.numel() * 4 < need:
-        raise ValueError(f"workspace must hold >= {need} bytes")
-    st = lib.fa_decode_paged(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
-                             _ptr(seq_lens), _ptr(o), _ptr(lse), _ptr(workspace), B, H, d, bs,
-                             block_tables.shape[1], nblk, float(scale),
-                             ctypes.c_void_p(_stream_handle(stream, q.device)))
+    return B, H, d, nblk, bs
+
+
+def fa_decode_paged_noalloc(q, k_pool, v_pool, block_tables, seq_lens, o, lse, scale,
+                            stream=None):
+    """fa_decode_paged without a workspace: the partial results live in the
+    library's fixed per-GPU buffer (DECODE_NOALLOC_SCRATCH_BYTES); for
+    callers that cannot allocate.  Calls that may overlap on one GPU race."""
+    lib = load_library()
+    B, H, d, nblk, bs = _check_decode(q, k_pool, v_pool, block_tables, seq_lens, o, lse)
+    st = lib.fa_decode_paged_noalloc(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables),
+                                     _ptr(seq_lens), _ptr(o), _ptr(lse), B, H, d, bs,
+                                     block_tables.shape[1], nblk, float(scale),
+                                     ctypes.c_void_p(_stream_handle(stream, q.device)))
     if st != FA_OK:
         raise FaError(st, fa_strerror(st))
-
 
 def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, dp_rowsum, scale, mask_kind=FA_MASK_NONE,
            kv_lens=None, stream=None):

@@ -25,8 +25,17 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "fa_api.h"
 #include "fa_device.h"
+
+// Scratch of fa_decode_paged_noalloc: the per-chunk partial results between
+// its two kernels live here instead of in a caller workspace.  Every GPU the
+// library runs on holds its own copy until the process ends; the host side
+// reaches it only through the device address hipGetSymbolAddress returns.
+static __device__ __align__(256) float scratch[FA_DECODE_NOALLOC_SCRATCH_BYTES / sizeof(float)];
 
 namespace {
 
@@ -234,17 +243,19 @@ extern "C" size_t fa_decode_paged_workspace_bytes(int B, int H, int d, int block
   return (size_t)B * H * nsplit_of(block_size, max_blocks_per_seq) * (d + 2) * sizeof(float);
 }
 
-extern "C" int fa_decode_paged(const void* q, const void* k_pool, const void* v_pool,
-                               const int32_t* block_tables, const int32_t* seq_lens, void* o,
-                               float* lse, float* workspace, int B, int H, int d, int block_size,
-                               int max_blocks_per_seq, int num_blocks, float scale,
-                               void* stream) {
-  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !o || !lse || !workspace)
+namespace {
+
+// Argument checks shared by both decode entry points (everything but the
+// workspace).
+int check_decode(const void* q, const void* k_pool, const void* v_pool,
+                 const int32_t* block_tables, const int32_t* seq_lens, const void* o,
+                 const float* lse, int B, int H, int d, int block_size, int max_blocks_per_seq,
+                 int num_blocks, float scale) {
+  if (!q || !k_pool || !v_pool || !block_tables || !seq_lens || !o || !lse)
     return FA_ERR_INVALID_ARG;
   if (((uintptr_t)q | (uintptr_t)k_pool | (uintptr_t)v_pool | (uintptr_t)o) & 15u)
     return FA_ERR_INVALID_ARG;
-  if (((uintptr_t)block_tables | (uintptr_t)seq_lens | (uintptr_t)lse | (uintptr_t)workspace) &
-      3u)
+  if (((uintptr_t)block_tables | (uintptr_t)seq_lens | (uintptr_t)lse) & 3u)
     return FA_ERR_INVALID_ARG;
   if (B < 1 || H < 1 || max_blocks_per_seq < 1 || num_blocks < 1) return FA_ERR_INVALID_ARG;
   if (block_size < 8 || block_size % 8 != 0 || block_size > 65536) return FA_ERR_INVALID_ARG;
@@ -254,6 +265,15 @@ extern "C" int fa_decode_paged(const void* q, const void* k_pool, const void* v_
   if (B > 65535 || H > 65535 || nsplit > 0x7fffffffLL ||
       (long long)block_size * max_blocks_per_seq > 0x7fffffffLL)
     return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+// Enqueues the split and combine kernels with `workspace` as their scratch
+// (arguments already checked).
+int launch_decode(const void* q, const void* k_pool, const void* v_pool,
+                  const int32_t* block_tables, const int32_t* seq_lens, void* o, float* lse,
+                  float* workspace, int B, int H, int d, int block_size, int max_blocks_per_seq,
+                  int num_blocks, float scale, void* stream) {
   DecParams p;
   p.q = q;
   p.kp = k_pool;
@@ -267,10 +287,10 @@ extern "C" int fa_decode_paged(const void* q, const void* k_pool, const void* v_
   p.bs = block_size;
   p.max_blocks = max_blocks_per_seq;
   p.num_blocks = num_blocks;
-  p.nsplit = (int)nsplit;
+  p.nsplit = nsplit_of(block_size, max_blocks_per_seq);
   p.c = scale * kLog2e;
   hipStream_t s = (hipStream_t)stream;
-  const dim3 g1((unsigned)nsplit, (unsigned)H, (unsigned)B);
+  const dim3 g1((unsigned)p.nsplit, (unsigned)H, (unsigned)B);
   if (d == 128) hipLaunchKernelGGL((fa_decode_split_kernel<128>), g1, dim3(kDecThreads), 0, s, p);
   else hipLaunchKernelGGL((fa_decode_split_kernel<64>), g1, dim3(kDecThreads), 0, s, p);
   if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
@@ -278,4 +298,65 @@ extern "C" int fa_decode_paged(const void* q, const void* k_pool, const void* v_
   if (d == 128) hipLaunchKernelGGL((fa_decode_combine_kernel<128>), g2, dim3(128), 0, s, p);
   else hipLaunchKernelGGL((fa_decode_combine_kernel<64>), g2, dim3(64), 0, s, p);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+// Device address of the current GPU's copy of `scratch`, looked up once per
+// device (with that device current) and kept; nullptr if the runtime cannot
+// give it.
+constexpr int kMaxDevices = 256;
+std::atomic<float*> scratch_ptr[kMaxDevices];
+std::mutex scratch_mu;
+
+float* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  float* ptr = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  ptr = scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!ptr) {
+    void* addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    ptr = (float*)addr;
+    scratch_ptr[dev].store(ptr, std::memory_order_release);
+  }
+  return ptr;
+}
+
+}  // namespace
+
+extern "C" int fa_decode_paged(const void* q, const void* k_pool, const void* v_pool,
+                               const int32_t* block_tables, const int32_t* seq_lens, void* o,
+                               float* lse, float* workspace, int B, int H, int d, int block_size,
+                               int max_blocks_per_seq, int num_blocks, float scale,
+                               void* stream) {
+  if (!workspace || ((uintptr_t)workspace & 3u)) return FA_ERR_INVALID_ARG;
+  const int st = check_decode(q, k_pool, v_pool, block_tables, seq_lens, o, lse, B, H, d,
+                              block_size, max_blocks_per_seq, num_blocks, scale);
+  if (st != FA_OK) return st;
+  return launch_decode(q, k_pool, v_pool, block_tables, seq_lens, o, lse, workspace, B, H, d,
+                       block_size, max_blocks_per_seq, num_blocks, scale, stream);
+}
+
+extern "C" int fa_decode_paged_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                                       const int32_t* block_tables, const int32_t* seq_lens,
+                                       void* o, float* lse, int B, int H, int d, int block_size,
+                                       int max_blocks_per_seq, int num_blocks, float scale,
+                                       void* stream) {
+  const int st = check_decode(q, k_pool, v_pool, block_tables, seq_lens, o, lse, B, H, d,
+                              block_size, max_blocks_per_seq, num_blocks, scale);
+  if (st != FA_OK) return st;
+  if (fa_decode_paged_workspace_bytes(B, H, d, block_size, max_blocks_per_seq) >
+      FA_DECODE_NOALLOC_SCRATCH_BYTES)
+    return FA_ERR_SCRATCH;
+  float* ws = scratch_on_current_device();
+  if (!ws) return FA_ERR_HIP;
+  return launch_decode(q, k_pool, v_pool, block_tables, seq_lens, o, lse, ws, B, H, d,
+                       block_size, max_blocks_per_seq, num_blocks, scale, stream);
 }

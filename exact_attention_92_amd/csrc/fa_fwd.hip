@@ -848,6 +848,8 @@ extern "C" const char* fa_strerror(int status) {
     case FA_ERR_UNSUPPORTED:
       return "unsupported head dimension (bf16 forward: 32, 64, 96, 128, 256; others: 64, 128)";
     case FA_ERR_HIP: return "HIP launch failure";
+    case FA_ERR_SCRATCH:
+      return "the call needs more scratch than the fixed buffer of the no-allocation entry point";
     default: return "unknown status";
   }
 }

@@ -80,7 +80,9 @@ enum {
   FA_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size, bad mask bits,
                               non-finite scale, padding without kv_lens */
   FA_ERR_UNSUPPORTED = -2, /* head dimension the entry point does not support */
-  FA_ERR_HIP = -3          /* the kernel launch failed */
+  FA_ERR_HIP = -3,         /* the kernel launch failed */
+  FA_ERR_SCRATCH = -4      /* needs more scratch than the no-allocation entry
+                              point's fixed buffer holds */
 };
 
 /* bfloat16 forward.  q, k, v, o: bf16 [B, H, N, d]; lse: float32 [B, H, N].
@@ -205,6 +207,28 @@ int fa_decode_paged(const void* q, const void* k_pool, const void* v_pool,
                     const int32_t* block_tables, const int32_t* seq_lens, void* o,
                     float* lse, float* workspace, int B, int H, int d, int block_size,
                     int max_blocks_per_seq, int num_blocks, float scale, void* stream);
+
+/* The same decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * no workspace argument; the per-chunk partial results live in a
+ * fixed-size buffer the library holds in each GPU's memory (a file-scope
+ * device array of FA_DECODE_NOALLOC_SCRATCH_BYTES, looked up once per
+ * device on the first call made with that device current).  The call
+ * allocates nothing.
+ *  - Arguments as for fa_decode_paged, without workspace.
+ *  - Returns FA_ERR_SCRATCH (and enqueues nothing) when
+ *    fa_decode_paged_workspace_bytes() of the same sizes exceeds
+ *    FA_DECODE_NOALLOC_SCRATCH_BYTES (16 MiB; B = 32, H = 32, d = 128 with
+ *    8192 cached tokens per request needs 8.5 MB).
+ *  - Every call on one GPU uses that GPU's single buffer: calls that may
+ *    run at the same time on one GPU (different streams, or overlapping
+ *    graph launches) race and must not be issued.  Nothing in the buffer
+ *    needs to start at zero; it keeps the last call's partial results. */
+#define FA_DECODE_NOALLOC_SCRATCH_BYTES (16u << 20)
+int fa_decode_paged_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* block_tables, const int32_t* seq_lens, void* o,
+                            float* lse, int B, int H, int d, int block_size,
+                            int max_blocks_per_seq, int num_blocks, float scale, void* stream);
 
 /* bfloat16 backward: the gradients of the attention above with respect to
  * q, k and v, given the upstream gradient dout = dL/dO.  With P the softmax

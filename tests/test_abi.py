@@ -26,9 +26,9 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared() == ["fa_bwd", "fa_decode_paged", "fa_decode_paged_workspace_bytes",
-                           "fa_fwd", "fa_fwd_f32", "fa_fwd_fp8", "fa_fwd_general",
-                           "fa_fwd_varlen", "fa_strerror"]
+    assert _declared() == ["fa_bwd", "fa_decode_paged", "fa_decode_paged_noalloc",
+                           "fa_decode_paged_workspace_bytes", "fa_fwd", "fa_fwd_f32",
+                           "fa_fwd_fp8", "fa_fwd_general", "fa_fwd_varlen", "fa_strerror"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -41,7 +41,8 @@ def test_library_exports_every_declared_symbol(lib):
 def test_strerror(lib):
     import exact_attention_92_amd as fa
     assert fa.fa_strerror(0) == "ok"
-    for st in (fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_HIP, 12345):
+    for st in (fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_HIP, fa.FA_ERR_SCRATCH,
+               12345):
         assert isinstance(fa.fa_strerror(st), str) and fa.fa_strerror(st)
 
 
@@ -150,6 +151,34 @@ def test_decode_invalid_arguments_are_rejected_before_launch(lib):
     assert call(d=96) == fa.FA_ERR_UNSUPPORTED
     assert lib.fa_decode_paged_workspace_bytes(2, 2, 128, 64, 4) == 2 * 2 * 1 * 130 * 4
     assert lib.fa_decode_paged_workspace_bytes(2, 2, 96, 64, 4) == 0
+
+
+def test_decode_noalloc_rejects_before_touching_a_device(lib):
+    """The no-allocation decode checks its arguments, then the size of its
+    partial results against the fixed buffer, before it looks up the device
+    (so these need no GPU)."""
+    import exact_attention_92_amd as fa
+    bad = fa.FA_ERR_INVALID_ARG
+    good = [0x1000 * (i + 1) for i in range(7)]
+
+    def call(ptrs=good, B=2, H=2, d=128, bs=64, mb=4, nb=8, scale=0.1):
+        return lib.fa_decode_paged_noalloc(
+            *[ctypes.c_void_p(p) if p is not None else None for p in ptrs], B, H, d, bs, mb, nb,
+            ctypes.c_float(scale), None)
+    for i in range(7):
+        p = list(good)
+        p[i] = None
+        assert call(p) == bad, i
+        p[i] = good[i] + (8 if i in (0, 1, 2, 5) else 2)
+        assert call(p) == bad, i
+    assert call(B=0) == bad and call(bs=12) == bad and call(scale=float("nan")) == bad
+    assert call(d=96) == fa.FA_ERR_UNSUPPORTED
+    # The partial results must fit in the 16 MiB buffer: 32 x 32 x 128 with
+    # 8192-token tables fits (8.5 MB), 64 x 32 x 128 does not (17.0 MB).
+    assert lib.fa_decode_paged_workspace_bytes(32, 32, 128, 64, 128) <= fa.DECODE_NOALLOC_SCRATCH_BYTES
+    assert lib.fa_decode_paged_workspace_bytes(64, 32, 128, 64, 128) > fa.DECODE_NOALLOC_SCRATCH_BYTES
+    assert call(B=64, H=32, mb=128) == fa.FA_ERR_SCRATCH
+    assert "scratch" in fa.fa_strerror(fa.FA_ERR_SCRATCH)
 
 
 def test_general_invalid_arguments_are_rejected_before_launch(lib):
