@@ -37,7 +37,8 @@ METRIC_BWD = "bwd attention TFLOP/s (bf16, N=4096 d=128 causal) and % of MFMA pe
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "fp8": 5000.0}   # MI355X dense MFMA peaks
 CSRC = os.path.join(ROOT, "exact_attention_92_amd", "csrc")
 # Sources each pass's kernels are built from (the PMC summaries record their hash).
-KERNEL_SRCS = {"fwd": ["fa_fwd.hip"], "bwd": ["fa_bwd.hip", "fa_bwd_kernels.h", "fa_device.h"],
+KERNEL_SRCS = {"fwd": ["fa_fwd.hip", "fa_device.h"],
+               "bwd": ["fa_bwd.hip", "fa_bwd_kernels.h", "fa_device.h"],
                "fp8": ["fa_fwd_fp8.hip", "fa_device.h"],
                "decode": ["fa_decode.hip", "fa_device.h"]}
 PMC_SUMMARY = {"fwd": os.path.join(ROOT, "profiles", "fa_fwd_bf16_b2h32_n4096_d128_causal_pmc.md"),

@@ -69,8 +69,11 @@ def compare(O, L, Or, Lr, dtype, what=""):
     nrm = np.linalg.norm(Or)
     stats["o_relf"] = float(np.linalg.norm(O - Or) / nrm) if nrm > 0 else 0.0
     stats["lse_abs"] = float(np.abs(L[~empty] - Lr[~empty]).max(initial=0.0))
-    say(f"  {what}: max|dO|={stats['o_abs']:.3e} relF={stats['o_relf']:.3e} "
-        f"max|dLSE|={stats['lse_abs']:.3e}")
+    def room(k):   # share of the bar still unused (negative: over the bar)
+        return "" if tol[k] is None else f" ({100.0 * (1.0 - stats[k] / tol[k]):.0f}% headroom)"
+    say(f"  {what}: max|dO|={stats['o_abs']:.3e}{room('o_abs')} "
+        f"relF={stats['o_relf']:.3e}{room('o_relf')} "
+        f"max|dLSE|={stats['lse_abs']:.3e}{room('lse_abs')}")
     assert stats["o_abs"] <= tol["o_abs"], (what, stats)
     if tol["o_relf"] is not None:
         assert stats["o_relf"] <= tol["o_relf"], (what, stats)

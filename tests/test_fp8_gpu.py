@@ -118,6 +118,16 @@ def test_d64_workload_shapes(mask):
 
 
 @pytest.mark.parametrize("d", [64, 128])
+def test_causal_items_all_resident(d):
+    """B*H = 64 causal heads of 1024 rows: every work item fits on the chip at
+    once, so the work order visits 8 heads per XCD group (the head-group
+    rule's second branch), not 4."""
+    x = make_raw(4, 16, 1024, d, "fp8", seed=4160 + d, q_mult=2.0)
+    O, L = run_fp8(x, d ** -0.5, MASK_CAUSAL)
+    compare_fp8(O, L, oracle(x, d ** -0.5, MASK_CAUSAL), f"B4 H16 N1024 d{d} causal", bulk=True)
+
+
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N", [1, 4, 63, 65, 127, 129, 1000])
 def test_ragged_lengths_all_masks(d, N):
     x = make_raw(2, 3, N, d, "fp8", seed=3000 + N + d, q_mult=2.0,

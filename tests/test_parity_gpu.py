@@ -2,7 +2,8 @@
 
 Every test here runs the kernels through the C ABI (ctypes binding) and
 compares element by element with the fp64 oracle; the N = 65536 workload is
-compared on sampled rows plus a closed form that holds at any size.  Output
+compared on every element, on sampled rows, and against a closed form that
+holds at any size.  Output
 buffers are pre-filled with NaN so an unwritten element fails.
 """
 import json
@@ -56,6 +57,37 @@ def test_long_context_sampled_rows():
     rows = np.unique(np.r_[0:130, g.integers(0, wl.N, 300), wl.N - 130:wl.N])
     Or, Lr = _oracle(x, wl.scale, wl.mask_kind, rows=rows)
     compare(O[:, :, rows], L[:, :, rows], Or, Lr, wl.dtype, wl.name + " sampled")
+
+
+def test_long_context_full_tensor():
+    """Every element of the N = 65536 workload (8 heads x 65536 rows) against
+    the oracle; the host computes the oracle's rows in chunks of 4096 per
+    head, in parallel (each chunk is the oracle's own arithmetic)."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+    wl = WORKLOADS["bf16_b1h8_n65536_d128_causal"]
+    say(f"[parity] {wl.name} (full tensor)")
+    x = make_inputs(wl)
+    O, L = run_gpu(x, wl.scale, wl.mask_kind)
+    q, k, v = (to_f64(x[n]) for n in "qkv")
+    Or, Lr = np.full_like(O, np.nan), np.full_like(L, np.nan)
+    step = 4096
+
+    def chunk(unit):
+        b, h, r0 = unit
+        rows = np.arange(r0, min(wl.N, r0 + step))
+        o, lse = attention_ref(q, k, v, wl.scale, wl.mask_kind, x.get("kv_lens"), rows=rows,
+                               heads=[(b, h)])
+        Or[b, h, rows], Lr[b, h, rows] = o[b, h], lse[b, h]
+
+    units = [(b, h, r0) for b in range(wl.B) for h in range(wl.H)
+             for r0 in range(wl.N - step, -1, -step)]      # longest rows first
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    with threadpool_limits(1), ThreadPoolExecutor(workers) as ex:
+        list(ex.map(chunk, units))
+    compare(O, L, Or, Lr, wl.dtype, wl.name + " full tensor")
 
 
 @pytest.mark.parametrize("d", [64, 128])
