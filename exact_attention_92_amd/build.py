@@ -54,8 +54,20 @@ def _run(cmd, verbose):
         print(err, file=sys.stderr)
 
 
+# The d = 128 forward's block loop is an inline-asm program written by a
+# generator beside the sources (its output is not kept in version control).
+GENERATORS = [os.path.join(PKG, "csrc", "gen_fwd_d128_loop.py")]
+
+
 def build(verbose: bool = False) -> str:
-    """Compile libfa92.so (always recompiles) and return its path."""
+    """Write the generated kernel bodies, compile libfa92.so (always
+    recompiles) and return its path."""
+    for gen in GENERATORS:
+        if verbose:
+            print(f"{sys.executable} {gen}", flush=True)
+        res = subprocess.run([sys.executable, gen], capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"{os.path.basename(gen)} failed:\n{res.stdout}{res.stderr}")
     tmp = LIB + ".tmp"
     objs = []
     for src in SRCS:

@@ -65,6 +65,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include <algorithm>
 #include <atomic>
@@ -485,6 +486,140 @@ void fa_fwd_bf16_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16, d = 128, contiguous self-attention, scale > 0: 64 query rows per wave
+// ---------------------------------------------------------------------------
+// Four waves (one per SIMD), 256 query rows per work item.  Each K and V^T
+// operand read from LDS feeds the MFMAs of two 32-row tiles, and the softmax
+// of one key block runs beside the MFMAs of the neighbouring blocks inside
+// one wave's instruction stream.  The block loop is one inline-asm program
+// (fa_fwd_d128_loop.inc, written by gen_fwd_d128_loop.py, which documents the
+// pipeline and the register plan); this function maps work items, computes
+// the per-item scalars and lane offsets and hands them to it.
+//
+// LDS: three K slots, then three V slots, 20 KiB each.  K rows are 272 bytes
+// apart and V rows 320, which makes the K operand reads (ds_read_b128) and
+// the transposing V^T reads (ds_read_b64_tr_b16) free of bank conflicts.
+// K and V blocks are staged with direct-to-LDS buffer loads: each wave
+// instruction writes 1 KiB of the padded slot image in lane order, and each
+// lane's source offset puts its 16 bytes where they belong (pad positions
+// read past the buffer range and receive zeros).
+constexpr int kD128Slot = 20480;
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
+void fa_fwd_d128_kernel(Params p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[6 * kD128Slot];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31;
+  const int hf = lane >> 5;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds;
+
+  // Staging: instruction u of this wave fills bytes [1024 (wave + 4u), +1024)
+  // of a slot.
+  uint32_t ko[5], vo[5];
+#pragma unroll
+  for (int u = 0; u < 5; ++u) {
+    const int pb = (wave + 4 * u) * 1024 + 16 * lane;
+    const int kr = pb / 272, kc = pb % 272, vr = pb / 320, vc = pb % 320;
+    ko[u] = (kr < 64 && kc < 256) ? (uint32_t)(kr * 256 + kc) : kOutOfRange;
+    vo[u] = (vr < 64 && vc < 256) ? (uint32_t)(vr * 256 + vc) : kOutOfRange;
+  }
+  // K operand of S^T = K Q^T: row row_perm(n) of a 32-key tile, d 8hf..8hf+7
+  // of each 16-wide step.  V^T operand: lanes 16g + j address V row
+  // 8(g/2) + j/4 (+ 16 pc + 4 half), columns 16(g%2) + 4(j%4) (+ 32 dt); the
+  // transposing read hands lane 16g + j the 4 keys of column 16(g%2) + j.
+  const uint32_t kaddr = lds0 + (uint32_t)(row_perm(n) * 272 + 16 * hf);
+  const int g = lane >> 4, j = lane & 15;
+  const uint32_t vaddr =
+      lds0 + 3 * kD128Slot + (uint32_t)((8 * (g >> 1) + (j >> 2)) * 320 + 32 * (g & 1) + 8 * (j & 3));
+  const uint32_t ldsk = __builtin_amdgcn_readfirstlane(lds0 + 1024u * wave);
+  const uint32_t ldsv = __builtin_amdgcn_readfirstlane(lds0 + 3 * kD128Slot + 1024u * wave);
+
+  const bool causal = p.causal != 0;
+  const int N = p.N;
+  const int P = gridDim.x, G = p.items;
+  const bool lanes8 = G % 8 == 0 && P % 8 == 0;
+  const int L8 = lanes8 ? 8 : 1;
+  const int lx = blockIdx.x % L8, mx = blockIdx.x / L8, Pm = P / L8, Gm = G / L8;
+  for (int round = 0;; ++round) {
+    const int idx = round * Pm + ((round & 1) ? Pm - 1 - mx : mx);
+    if (idx >= Gm) break;
+    int bh, qb;
+    map_work(p.nqb, causal, p.hg, false, idx * L8 + lx, p.items, bh, qb);
+    const int b = bh / p.H;
+    const size_t hoff = (size_t)bh * (size_t)N * 128;
+    const uint64_t qa = (uint64_t)((const uint16_t*)p.q + hoff);
+    const uint64_t ka = (uint64_t)((const uint16_t*)p.k + hoff);
+    const uint64_t va = (uint64_t)((const uint16_t*)p.v + hoff);
+    const uint64_t oa = (uint64_t)((uint16_t*)p.o + hoff);
+    const uint64_t la = (uint64_t)(p.lse + (size_t)bh * N);
+    int n_vis = N;
+    if (p.kv_lens) {
+      const int kl = p.kv_lens[b];
+      n_vis = kl < 0 ? 0 : (kl > N ? N : kl);
+    }
+    n_vis = __builtin_amdgcn_readfirstlane(n_vis);
+    const int q0 = qb * 256;
+    const int qw0 = q0 + 64 * wave;
+    const int kend = causal ? min(n_vis, q0 + 256) : n_vis;
+    const int nblk = __builtin_amdgcn_readfirstlane((kend + 63) / 64);
+    // Last key block this wave visits (-1: none); only it can hold hidden keys.
+    int jlast = -1;
+    if (qw0 < N) {
+      const int kv = causal ? min(n_vis, qw0 + 64) : n_vis;
+      jlast = (kv + 63) / 64 - 1;
+    }
+    jlast = __builtin_amdgcn_readfirstlane(jlast);
+    // Mask of that block: register index i (0..63) of a lane is hidden when
+    // i > lim (key kb + i + 8hf against the lane's row).
+    const int kb = 64 * (jlast > 0 ? jlast : 0);
+    const int rowA = qw0 + n, rowB = qw0 + 32 + n;
+    const int limA = (causal ? min(rowA, n_vis - 1) : n_vis - 1) - kb - 8 * hf;
+    const int limB = (causal ? min(rowB, n_vis - 1) : n_vis - 1) - kb - 8 * hf;
+    const uint32_t qoff0 = (uint32_t)rowA * 256u + 16u * hf, qoff1 = qoff0 + 8192u;
+    const uint32_t ooff0 = (uint32_t)rowA * 256u + 8u * hf, ooff1 = ooff0 + 8192u;
+    const uint32_t loff0 = hf ? kOutOfRange : (uint32_t)rowA * 4u;
+    const uint32_t loff1 = hf ? kOutOfRange : (uint32_t)rowB * 4u;
+    const uint32_t nbytes = (uint32_t)N * 256u, vbytes = (uint32_t)n_vis * 256u;
+    const uint32_t lbytes = (uint32_t)N * 4u;
+#ifdef FA_D128_DEBUG
+#ifdef FA_D128_PROFILE
+    const uint32_t dbgoff = lane == 0 ? (uint32_t)((qb * 4 + wave) * 8 * 256) : kOutOfRange;
+#else
+    const uint32_t dbgoff = qb == 0 ? (uint32_t)(wave * 230 * 256 + lane * 4) : kOutOfRange;
+#endif
+#define FA_D128_DBG_OPERAND , [dbg] "v"(dbgoff)
+#define FA_D128_BODY "fa_fwd_d128_loop_debug.inc"
+#define FA_D128_CLOBBERS "fa_fwd_d128_clobbers_debug.inc"
+#else
+#define FA_D128_DBG_OPERAND
+#define FA_D128_BODY "fa_fwd_d128_loop.inc"
+#define FA_D128_CLOBBERS "fa_fwd_d128_clobbers.inc"
+#endif
+    asm volatile(
+#include FA_D128_BODY
+        :
+        : [klo] "s"((uint32_t)ka), [khi] "s"((uint32_t)(ka >> 32)), [kbytes] "s"(nbytes),
+          [vlo] "s"((uint32_t)va), [vhi] "s"((uint32_t)(va >> 32)), [vbytes] "s"(vbytes),
+          [qlo] "s"((uint32_t)qa), [qhi] "s"((uint32_t)(qa >> 32)), [qbytes] "s"(nbytes),
+          [olo] "s"((uint32_t)oa), [ohi] "s"((uint32_t)(oa >> 32)),
+          [llo] "s"((uint32_t)la), [lhi] "s"((uint32_t)(la >> 32)), [lbytes] "s"(lbytes),
+          [nblk] "s"(nblk), [jlast] "s"(jlast), [c] "s"(p.c), [ldsk] "s"(ldsk), [ldsv] "s"(ldsv),
+          [ko0] "v"(ko[0]), [ko1] "v"(ko[1]), [ko2] "v"(ko[2]), [ko3] "v"(ko[3]),
+          [ko4] "v"(ko[4]), [vo0] "v"(vo[0]), [vo1] "v"(vo[1]), [vo2] "v"(vo[2]),
+          [vo3] "v"(vo[3]), [vo4] "v"(vo[4]), [qoff0] "v"(qoff0), [qoff1] "v"(qoff1),
+          [ooff0] "v"(ooff0), [ooff1] "v"(ooff1), [loff0] "v"(loff0), [loff1] "v"(loff1),
+          [kaddr] "v"(kaddr), [vaddr] "v"(vaddr), [limA] "v"(limA), [limB] "v"(limB)
+          FA_D128_DBG_OPERAND
+        :
+#include FA_D128_CLOBBERS
+    );
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 kernel (v_mfma_f32_32x32x2_f32; no narrowing anywhere)
 // ---------------------------------------------------------------------------
 constexpr int kBN32 = 32;
@@ -689,6 +824,27 @@ void launch_one(hipStream_t s, Params p) {
                      s, p);
 }
 
+// The 64-rows-per-wave d = 128 kernel: at most as many workgroups as the chip
+// holds (one per CU), each looping over 256-row items in snake order.
+void launch_d128(hipStream_t s, Params p) {
+  static std::atomic<long long> cache{0};
+  const long long resident = resident_workgroups(fa_fwd_d128_kernel, 256, cache);
+  p.hg = head_group(p.causal != 0, p.items, resident);
+  const long long cap = resident > 0 ? resident : kCUs;
+  const long long grid = std::min<long long>(p.items, cap);
+  hipLaunchKernelGGL(fa_fwd_d128_kernel, dim3((unsigned)grid), dim3(256), 0, s, p);
+}
+
+// FA92_FWD_D128=0 in the environment sends d = 128 to the 32-rows-per-wave
+// kernel as well (read once per process; for side-by-side comparisons).
+bool use_d128_kernel() {
+  static const int on = [] {
+    const char* e = getenv("FA92_FWD_D128");
+    return (e && e[0] == '0') ? 0 : 1;
+  }();
+  return on != 0;
+}
+
 // 8-wave (256-row) workgroups when big, else 4-wave.
 template <int MODE>
 void launch_bf16(int d, bool big, hipStream_t s, const Params& p) {
@@ -718,6 +874,13 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
       check_args(q, k, v, o, lse, B, H, N, d, scale, mask_kind, kv_lens, 128, 256, true);
   if (st != FA_OK) return st;
   hipStream_t s = (hipStream_t)stream;
+  if (d == 128 && scale > 0.f && use_d128_kernel()) {
+    const int nqb = (N + 255) / 256;
+    Params p = make_params(q, k, v, o, lse, H, N, nqb, scale, mask_kind, kv_lens);
+    p.items = B * H * nqb;
+    launch_d128(s, p);
+    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+  }
   // 256-row workgroups (8 waves, one per CU) share each K/V tile among more
   // rows.  They are used when they fill the 256 CUs at least once (twice for
   // causal masks, whose query blocks differ in cost); otherwise 128-row
