@@ -471,11 +471,15 @@ def build(debug=False):
     # every block staged so far must have landed: after this barrier K(i),
     # V(i-1) and K(i+1) are visible to all waves (the end of iteration i reads
     # K(i+1) ahead of the next barrier)
-    e(f"{top}:", "s_waitcnt vmcnt(0)", *mark("vmwait"), "s_barrier", *mark("barrier"),
-      f"s_mov_b32 {s(SRT)}, {s(SR0)}", f"s_mov_b32 {s(SR0)}, {s(SR1)}",
-      f"s_mov_b32 {s(SR1)}, {s(SR2)}", f"s_mov_b32 {s(SR2)}, {s(SRT)}",
-      f"s_add_u32 {s(SMK)}, %[ldsk], {s(SR2)}", f"s_add_u32 {s(SMV)}, %[ldsv], {s(SR1)}",
-      f"v_add_u32_e32 {v(KRD)}, {s(SR0)}, %[kaddr]", f"v_add_u32_e32 {v(VRD)}, {s(SR2)}, %[vaddr]")
+    def opening():
+        """Barrier that opens an iteration, then the slot rotation."""
+        return ["s_waitcnt vmcnt(0)", *mark("vmwait"), "s_barrier", *mark("barrier"),
+                f"s_mov_b32 {s(SRT)}, {s(SR0)}", f"s_mov_b32 {s(SR0)}, {s(SR1)}",
+                f"s_mov_b32 {s(SR1)}, {s(SR2)}", f"s_mov_b32 {s(SR2)}, {s(SRT)}",
+                f"s_add_u32 {s(SMK)}, %[ldsk], {s(SR2)}", f"s_add_u32 {s(SMV)}, %[ldsv], {s(SR1)}",
+                f"v_add_u32_e32 {v(KRD)}, {s(SR0)}, %[kaddr]",
+                f"v_add_u32_e32 {v(VRD)}, {s(SR2)}, %[vaddr]"]
+    e(f"{top}:", *opening())
     # this wave's part of iteration i (jlast = its last key block, -1: none);
     # every variant stages its share of K(i+1) and V(i)
     labs = {k: prog.label(k) for k in ("first", "firstm", "st0", "st1", "last0", "last1",
@@ -509,14 +513,22 @@ def build(debug=False):
                 ("last1", 1, True, "plain", True, "masked", True, False),
                 ("tail0", 0, False, "masked", True, None, False, False),
                 ("tail1", 1, False, "masked", True, None, False, False)]
+    counted = prog.label("counted")
     for name, p, do_s, sm_b, do_pv, sm_a, pre, pre_next in variants:
         e(f"{labs[name]}:")
         e(*iteration(prog, p, do_s, sm_b, do_pv, sm_a, pre, pre_next))
-        e(f"s_branch {nxt}")
+        if name in ("st0", "st1"):
+            # steady state: while the next iteration is steady too, open it
+            # here and go straight to its code (the other parity)
+            e(*mark("idle"), f"s_add_u32 {s(SI)}, {s(SI)}, 1",
+              f"s_cmp_lt_i32 {s(SI)}, %[jlast]", f"s_cbranch_scc0 {counted}",
+              *opening(), *mark("loads"), f"s_branch {labs['st1' if name == 'st0' else 'st0']}")
+        else:
+            e(f"s_branch {nxt}")
     for p in (0, 1):
         e(f"{labs['idle%d' % p]}:", *stage("K"), *stage("V"), f"s_branch {nxt}")
-    e(f"{nxt}:", *mark("idle"), f"s_add_u32 {s(SI)}, {s(SI)}, 1", f"s_cmp_le_i32 {s(SI)}, %[nblk]",
-      f"s_cbranch_scc1 {top}")
+    e(f"{nxt}:", *mark("idle"), f"s_add_u32 {s(SI)}, {s(SI)}, 1",
+      f"{counted}:", f"s_cmp_le_i32 {s(SI)}, %[nblk]", f"s_cbranch_scc1 {top}")
     e(f"{done}:")
 
     # epilogue: O = acc / l (bf16), LSE = (m + log2 le) * ln 2; rows past N and
