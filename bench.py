@@ -37,7 +37,7 @@ METRIC_BWD = "bwd attention TFLOP/s (bf16, N=4096 d=128 causal) and % of MFMA pe
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "fp8": 5000.0}   # MI355X dense MFMA peaks
 CSRC = os.path.join(ROOT, "exact_attention_92_amd", "csrc")
 # Sources each pass's kernels are built from (the PMC summaries record their hash).
-KERNEL_SRCS = {"fwd": ["fa_fwd.hip", "fa_device.h"],
+KERNEL_SRCS = {"fwd": ["fa_fwd.hip", "fa_device.h", "gen_fwd_d128_loop.py"],
                "bwd": ["fa_bwd.hip", "fa_bwd_kernels.h", "fa_device.h"],
                "fp8": ["fa_fwd_fp8.hip", "fa_device.h"],
                "decode": ["fa_decode.hip", "fa_device.h"]}
@@ -47,6 +47,16 @@ PMC_SUMMARY = {"fwd": os.path.join(ROOT, "profiles", "fa_fwd_bf16_b2h32_n4096_d1
                "decode": os.path.join(ROOT, "profiles",
                                       "fa_decode_paged_b32h32_d128_bs64_len1k8k_pmc.md")}
 HBM_PEAK_GBS = 8000.0
+
+
+def fwd_kernel_name(wl, general):
+    """The forward kernel fa_fwd and friends dispatch this workload to."""
+    if wl.dtype == "bf16" and not general and wl.d == 128 and wl.scale > 0 \
+            and os.environ.get("FA92_FWD_D128", "1")[:1] != "0":
+        return "fa_fwd_d128_kernel"
+    name = {"bf16": "fa_fwd_bf16_kernel", "f32": "fa_fwd_f32_kernel",
+            "fp8": "fa_fwd_fp8_kernel"}[wl.dtype]
+    return name + (" (general layout)" if general else "")
 
 
 def kernel_source_hash(which="fwd"):
@@ -396,9 +406,7 @@ def main():
                    "flops_per_step": flops, "device": torch.cuda.get_device_name(dev)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": {"bf16": "fa_fwd_bf16_kernel", "f32": "fa_fwd_f32_kernel",
-                                "fp8": "fa_fwd_fp8_kernel"}[wl.dtype]
-                     + (" (general layout)" if general else ""),
+                     "kernel": fwd_kernel_name(wl, general or varlen),
                      "avg_launch_us": round(avg_launch_ms * 1e3, 2),
                      "min_launch_us": round(min(launch_ms) * 1e3, 2)},
         "cpu_baseline": None,

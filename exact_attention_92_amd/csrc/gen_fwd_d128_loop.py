@@ -445,6 +445,17 @@ def build(debug=False):
                              (SQ, "qlo", "qhi", "qbytes"), (SL, "llo", "lhi", "lbytes")):
         e(f"s_mov_b32 {s(base)}, %[{lo}]", f"s_and_b32 {s(base + 1)}, %[{hi}], 0xffff",
           f"s_mov_b32 {s(base + 2)}, %[{nb}]", f"s_mov_b32 {s(base + 3)}, 0x20000")
+    # K(0), K(1) and V(0) into slot 0, 1 and 0 first (their latency overlaps
+    # the rest of the set-up); the loop's slot rotation then starts from
+    # (0, 1, 2)
+    done = prog.label("done")
+    staged = prog.label("staged")
+    e("s_cmp_gt_i32 %[nblk], 0", f"s_cbranch_scc0 {staged}")
+    e(*stage("K", "%[ldsk]"))
+    e(f"s_add_u32 {s(SMK)}, %[ldsk], {SLOT}", *stage("K"))
+    e(*stage("V", "%[ldsv]"))
+    e(f"s_mov_b32 {s(SR0)}, {2 * SLOT}", f"s_mov_b32 {s(SR1)}, 0", f"s_mov_b32 {s(SR2)}, {SLOT}")
+    e(f"{staged}:")
     # Q rows of both tiles into AGPRs (B operand of S^T = K Q^T)
     for tile, qo in (("A", "%[qoff0]"), ("B", "%[qoff1]")):
         for ks in range(8):
@@ -456,14 +467,7 @@ def build(debug=False):
         e(f"v_mov_b32_e32 {v(M[tile])}, 0xff800000", f"v_mov_b32_e32 {v(LE[tile])}, 0")
     for r in list(range(ACC["A"], ACC["B"] + 64)) + list(range(LACC["A"], LACC["B"] + 16)):
         e(f"v_accvgpr_write_b32 {a(r)}, 0")
-    done = prog.label("done")
     e("s_cmp_gt_i32 %[nblk], 0", f"s_cbranch_scc0 {done}")
-    # K(0), K(1) and V(0) into slot 0, 1 and 0; the loop's slot rotation then
-    # starts from (0, 1, 2)
-    e(*stage("K", "%[ldsk]"))
-    e(f"s_add_u32 {s(SMK)}, %[ldsk], {SLOT}", *stage("K"))
-    e(*stage("V", "%[ldsv]"))
-    e(f"s_mov_b32 {s(SR0)}, {2 * SLOT}", f"s_mov_b32 {s(SR1)}, 0", f"s_mov_b32 {s(SR2)}, {SLOT}")
     e(f"s_mov_b32 {s(SI)}, 0")
 
     top = prog.label("top")
