@@ -7,8 +7,8 @@ script before compiling.
 Why asm: the body is a software pipeline whose value is the exact interleave
 of matrix-core and vector work inside one wave -- the exponentials of one key
 block issue between the MFMAs of the next block's scores and of the previous
-block's P.V -- and a fixed register plan (O accumulators, row sums and Q in
-AGPRs; scores, probabilities and LDS operands in VGPRs) that the compiler
+block's P.V -- and a fixed register plan (O accumulators and Q in AGPRs;
+scores, probabilities, row sums and LDS operands in VGPRs) that the compiler
 does not keep.
 
 What it computes is the online softmax of the tiled exact attention forward
@@ -52,17 +52,17 @@ LE = {"A": 178, "B": 181}     # row sum of the fp32 probabilities (per lane half
 RE = {"A": 182, "B": 184}     # fp32 block sums, two partial sums each
 T = 186                       # slow-path / epilogue temporaries v[186:190]
 NINF = 191                    # -inf
-ONES4 = 192                   # v[192:195]: bf16 ones, the A operand of the row-sum MFMA
+ONES = 192                    # 0x3f803f80: a pair of bf16 ones
+# Row sums of the bf16-rounded probabilities (they normalise O), two partial
+# sums per lane and tile, accumulated with v_dot2c after the phase's last
+# MFMA: dot instructions do not overlap MFMAs, so inside the interleaved
+# stream they would stall it.
+LV = {"A": (177, 193), "B": (180, 194)}
 NVGPR = 206                   # v[0:205] are clobbered
 
 ACC = {"A": 0, "B": 64}       # O^T accumulators: a[0:63] tile A, a[64:127] tile B (dt at +16dt)
 QA = {"A": 128, "B": 160}     # Q tiles (MFMA B operand), ks at +4ks: a[128:191]
-# Row sums of the bf16-rounded probabilities (they normalise O), kept by the
-# matrix core: an all-ones 32x16 A operand times P^T gives every row of the
-# output the column sums of P^T, so register 0 of each lane holds its row's
-# complete sum (the VALU dot instructions would stall behind the MFMAs).
-LACC = {"A": 192, "B": 208}   # a[192:207], a[208:223]; only register 0 is read
-NAGPR = 224
+NAGPR = 192
 
 # SGPRs (clobbered): s[64:67] K rsrc (next block to stage), s[68:71] V rsrc,
 # s[72:75] Q / O rsrc, s[76:79] LSE rsrc, s80 block counter i, s81 scratch;
@@ -209,9 +209,9 @@ def slow_path(prog, tile, sreg, preg, back):
             c.append(f"v_mul_f32_e32 {v(ET + k)}, {v(t3)}, {v(ET + k)}")
         for k in range(8):
             c.append(f"v_accvgpr_write_b32 {a(acc + g + k)}, {v(ET + k)}")
-    c.append(f"v_accvgpr_read_b32 {v(ET)}, {a(LACC[tile])}")
-    c.append(f"v_mul_f32_e32 {v(ET)}, {v(t3)}, {v(ET)}")
-    c.append(f"v_accvgpr_write_b32 {a(LACC[tile])}, {v(ET)}")
+    c.append("s_nop 2")                      # partial sums were last written by dot instructions
+    for r in LV[tile]:
+        c.append(f"v_mul_f32_e32 {v(r)}, {v(t3)}, {v(r)}")
     c.append(f"v_mul_f32_e32 {v(LE[tile])}, {v(t3)}, {v(LE[tile])}")
     c.append(f"v_mov_b32_e32 {v(M[tile])}, {v(t2)}")
     c.append(f"v_cmp_eq_f32_e32 vcc, 0xff800000, {v(t2)}")
@@ -226,11 +226,15 @@ def check(prog, tile, sreg, preg):
     """Fast-path test of a tile's block sums; the slow path returns here."""
     back = prog.label("back" + tile)
     lab = slow_path(prog, tile, sreg, preg, back)
-    return [f"v_cmp_nge_f32_e32 vcc, {LIMIT_SUM}, {v(RE[tile])}",
-            "s_nop 1",
-            f"s_cbranch_vccnz {lab}",
-            f"v_add_f32_e32 {v(LE[tile])}, {v(LE[tile])}, {v(RE[tile])}",
-            f"{back}:"]
+    out = [f"v_cmp_nge_f32_e32 vcc, {LIMIT_SUM}, {v(RE[tile])}",
+           "s_nop 1",
+           f"s_cbranch_vccnz {lab}",
+           f"v_add_f32_e32 {v(LE[tile])}, {v(LE[tile])}, {v(RE[tile])}",
+           f"{back}:"]
+    # bf16-rounded row sums of this block's P^T into the two partial sums
+    for r in range(16):
+        out.append(f"v_dot2c_f32_bf16_e32 {v(LV[tile][r % 2])}, {v(ONES)}, {v(preg + r)}")
+    return out
 
 
 # ------------------------------------------------------- one loop iteration
@@ -377,11 +381,6 @@ def iteration(prog, p, do_s, sm_b, do_pv, sm_a, prefetched=False, prefetch_next=
                 acc = ACC[tile] + 16 * dt
                 y_mfma.append((k, f"v_mfma_f32_32x32x16_bf16 {a(acc, 16)}, {v(ring, 4)}, "
                                   f"{v(preg + 4 * pc, 4)}, {a(acc, 16)}"))
-            if dt == 3:
-                for tile, preg in (("A", P_A[1 - p]), ("B", P_B)):
-                    la = LACC[tile]
-                    y_mfma.append((k, f"v_mfma_f32_32x32x16_bf16 {a(la, 16)}, {v(ONES4, 4)}, "
-                                      f"{v(preg + 4 * pc, 4)}, {a(la, 16)}"))
         if sm_b:
             out.append("s_nop 4")            # P^T of tile B was just written by VALU
     y_valu = softmax_slots("A", S_A, P_A[p], M["A"], sm_a == "masked") if sm_a else []
@@ -461,11 +460,11 @@ def build(debug=False):
         for ks in range(8):
             e(f"buffer_load_dwordx4 {a(QA[tile] + 4 * ks, 4)}, {qo}, {s(SQ, 4)}, 0 offen "
               f"offset:{32 * ks}")
-    e(*[f"v_mov_b32_e32 {v(ONES4 + i)}, 0x3f803f80" for i in range(4)],
-      f"v_mov_b32_e32 {v(NINF)}, 0xff800000")
+    e(f"v_mov_b32_e32 {v(ONES)}, 0x3f803f80", f"v_mov_b32_e32 {v(NINF)}, 0xff800000",
+      *[f"v_mov_b32_e32 {v(r)}, 0" for t in ("A", "B") for r in LV[t]])
     for tile in ("A", "B"):
         e(f"v_mov_b32_e32 {v(M[tile])}, 0xff800000", f"v_mov_b32_e32 {v(LE[tile])}, 0")
-    for r in list(range(ACC["A"], ACC["B"] + 64)) + list(range(LACC["A"], LACC["B"] + 16)):
+    for r in range(ACC["A"], ACC["B"] + 64):
         e(f"v_accvgpr_write_b32 {a(r)}, 0")
     e("s_cmp_gt_i32 %[nblk], 0", f"s_cbranch_scc0 {done}")
     e(f"s_mov_b32 {s(SI)}, 0")
@@ -561,8 +560,11 @@ def build(debug=False):
         return prog
     for t, tile in enumerate(("A", "B")):
         t0, t1, t2, t3, t4 = T, T + 1, T + 2, T + 3, T + 4
-        e(f"v_accvgpr_read_b32 {v(t0)}, {a(LACC[tile])}",           # l
-          f"v_mov_b32_e32 {v(t2)}, {v(LE[tile])}", f"v_mov_b32_e32 {v(t3)}, {v(LE[tile])}",
+        e("s_nop 2", f"v_add_f32_e32 {v(t0)}, {v(LV[tile][0])}, {v(LV[tile][1])}",
+          f"v_mov_b32_e32 {v(t1)}, {v(t0)}", "s_nop 1",
+          f"v_permlane32_swap_b32_e32 {v(t0)}, {v(t1)}", "s_nop 1",
+          f"v_add_f32_e32 {v(t0)}, {v(t0)}, {v(t1)}")              # l
+        e(f"v_mov_b32_e32 {v(t2)}, {v(LE[tile])}", f"v_mov_b32_e32 {v(t3)}, {v(LE[tile])}",
           "s_nop 1",
           f"v_permlane32_swap_b32_e32 {v(t2)}, {v(t3)}",
           "s_nop 1",
