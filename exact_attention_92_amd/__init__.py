@@ -17,6 +17,8 @@ Names follow the C ABI of ``include/fa_api.h``:
 * ``fa_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, o, lse, scale,
   mask_kind=0, kv_lens=None, stream=None)`` -- E4M3 codes (uint8 tensors)
   with per-(batch, head) float32 scales; o is bf16
+* ``fa_fwd_fp8_tiled(...)`` -- the same with one q / k scale per 128 rows
+  (``q_descale``, ``k_descale`` float32 ``[B, H, ceil(N / 128)]``)
 * ``fa_decode_paged(q, k_pool, v_pool, block_tables, seq_lens, o, lse,
   workspace, scale, stream=None)`` and
   ``fa_decode_paged_workspace_bytes(B, H, d, block_size, max_blocks)``
@@ -44,7 +46,8 @@ FA_ERR_SCRATCH = -4
 DECODE_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa92.so")
-EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_general", "fa_fwd_varlen", "fa_fwd_fp8", "fa_bwd",
+EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_general", "fa_fwd_varlen", "fa_fwd_fp8",
+           "fa_fwd_fp8_tiled", "fa_bwd",
            "fa_decode_paged", "fa_decode_paged_noalloc", "fa_decode_paged_workspace_bytes",
            "fa_strerror")
 
@@ -77,8 +80,10 @@ def load_library():
     lib.fa_fwd_varlen.argtypes = [vp] * 7 + [i32] * 3 + [ctypes.c_int64] * 2 + [i32, f32, i32,
                                                                                i32, vp]
     lib.fa_fwd_varlen.restype = i32
-    lib.fa_fwd_fp8.argtypes = [vp] * 8 + [i32, i32, i32, i32, f32, i32, vp, vp]
-    lib.fa_fwd_fp8.restype = i32
+    for name in ("fa_fwd_fp8", "fa_fwd_fp8_tiled"):
+        fn = getattr(lib, name)
+        fn.argtypes = [vp] * 8 + [i32, i32, i32, i32, f32, i32, vp, vp]
+        fn.restype = i32
     lib.fa_decode_paged.argtypes = [vp] * 8 + [i32] * 6 + [f32, vp]
     lib.fa_decode_paged.restype = i32
     lib.fa_decode_paged_noalloc.argtypes = [vp] * 7 + [i32] * 6 + [f32, vp]
@@ -238,10 +243,11 @@ def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, sca
         raise FaError(st, fa_strerror(st))
 
 
-def fa_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, o, lse, scale, mask_kind=FA_MASK_NONE,
-               kv_lens=None, stream=None):
-    """E4M3 forward: q, k, v uint8 codes [B, H, N, d]; descales float32 [B, H];
-    writes o (bf16) and lse (float32)."""
+FP8_TILE = 128    # rows per scale tile of fa_fwd_fp8_tiled (FA_FP8_TILE)
+
+
+def _fp8_call(name, q, k, v, q_descale, k_descale, v_descale, o, lse, scale, mask_kind,
+              kv_lens, stream, qk_scales):
     import torch
     lib = load_library()
     _check("q", q, torch.uint8)    # E4M3 codes
@@ -252,17 +258,34 @@ def fa_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, o, lse, scale, mask_kin
     B, H, N, d = q.shape
     for nm, t in (("q_descale", q_descale), ("k_descale", k_descale), ("v_descale", v_descale)):
         _check(nm, t, torch.float32, device=q.device)
-        if t.numel() != B * H:
-            raise ValueError(f"{nm} must hold B * H = {B * H} scales")
+        want = qk_scales(B, H, N) if nm != "v_descale" else B * H
+        if t.numel() != want:
+            raise ValueError(f"{nm} must hold {want} scales")
     _check("o", o, torch.bfloat16, (B, H, N, d), q.device)
     _check("lse", lse, torch.float32, (B, H, N), q.device)
     _check_kv_lens(kv_lens, B, q.device)
-    st = lib.fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(q_descale), _ptr(k_descale),
-                        _ptr(v_descale), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
-                        int(mask_kind), _ptr(kv_lens),
-                        ctypes.c_void_p(_stream_handle(stream, q.device)))
+    st = getattr(lib, name)(_ptr(q), _ptr(k), _ptr(v), _ptr(q_descale), _ptr(k_descale),
+                            _ptr(v_descale), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
+                            int(mask_kind), _ptr(kv_lens),
+                            ctypes.c_void_p(_stream_handle(stream, q.device)))
     if st != FA_OK:
         raise FaError(st, fa_strerror(st))
+
+
+def fa_fwd_fp8(q, k, v, q_descale, k_descale, v_descale, o, lse, scale, mask_kind=FA_MASK_NONE,
+               kv_lens=None, stream=None):
+    """E4M3 forward: q, k, v uint8 codes [B, H, N, d]; descales float32 [B, H];
+    writes o (bf16) and lse (float32)."""
+    _fp8_call("fa_fwd_fp8", q, k, v, q_descale, k_descale, v_descale, o, lse, scale, mask_kind,
+              kv_lens, stream, lambda B, H, N: B * H)
+
+
+def fa_fwd_fp8_tiled(q, k, v, q_descale, k_descale, v_descale, o, lse, scale,
+                     mask_kind=FA_MASK_NONE, kv_lens=None, stream=None):
+    """E4M3 forward with per-tile Q and K scales: q_descale, k_descale float32
+    [B, H, ceil(N / 128)] (one per 128 rows), v_descale float32 [B, H]."""
+    _fp8_call("fa_fwd_fp8_tiled", q, k, v, q_descale, k_descale, v_descale, o, lse, scale,
+              mask_kind, kv_lens, stream, lambda B, H, N: B * H * (-(-N // FP8_TILE)))
 
 
 def fa_decode_paged_workspace_bytes(B, H, d, block_size, max_blocks):

@@ -97,9 +97,14 @@ struct P8Params {
   unsigned qsign;   // E4M3 sign flip applied to Q when scale < 0
   int causal;
   int hg;           // heads map_work visits together (head_group)
+  int nqt;          // per-tile scales: FA_FP8_TILE-row tiles per head (ceil(N / 128))
 };
 
-template <int D, int NW>
+// TILED: q_descale and k_descale hold one scale per FA_FP8_TILE rows of each
+// head (block quantization at tile granularity); a wave's 32 query rows lie
+// in one Q tile and a key block in one K tile, so the scales enter the logit
+// multiplier c per key block -- one scalar product per block.
+template <int D, int NW, bool TILED>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2)))
 void fa_fwd_fp8_kernel(P8Params p) {
   constexpr int kThreads = 64 * NW;
@@ -148,7 +153,11 @@ void fa_fwd_fp8_kernel(P8Params p) {
   const int nblk = (kend + BN - 1) / BN;
 
   // Logits in log2 units: s * |scale| * q_descale * k_descale * log2(e).
-  const float c = fmaxf(p.ascale * p.q_descale[bh] * p.k_descale[bh], kMinScale) * kLog2e;
+  static_assert(!TILED || BN <= FA_FP8_TILE, "a key block must lie in one scale tile");
+  const float cq = p.ascale * (TILED ? p.q_descale[(size_t)bh * p.nqt + min(qw0 / FA_FP8_TILE,
+                                                                             p.nqt - 1)]
+                                     : p.q_descale[bh]);
+  float c = fmaxf(cq * p.k_descale[bh], kMinScale) * kLog2e;
 
   // Q row of this lane: the B operand of S^T = K Q^T, bytes 64ks + 32hf + 0..31.
   i32x8_t qr[KS];
@@ -231,6 +240,8 @@ void fa_fwd_fp8_kernel(P8Params p) {
     const bool more = j + 1 < nblk;
     if (more) load_block(j + 1);
     const int kbase = j * BN;
+    if (TILED) c = fmaxf(cq * p.k_descale[(size_t)bh * p.nqt + kbase / FA_FP8_TILE], kMinScale) *
+                   kLog2e;
     if (!(causal && kbase > qw0 + 31)) {
       // S^T = K_j Q^T: register r of tile kt holds key kbase + 32kt +
       // 16(r/8) + 8hf + r%8 of this lane's query row.
@@ -327,20 +338,19 @@ void fa_fwd_fp8_kernel(P8Params p) {
   }
 }
 
-template <int D, int NW>
+template <int D, int NW, bool TILED>
 void launch_fp8(unsigned grid, hipStream_t s, P8Params p) {
   static std::atomic<long long> resident{0};
   p.hg = head_group(p.causal != 0, grid,
-                    resident_workgroups(fa_fwd_fp8_kernel<D, NW>, 64 * NW, resident));
-  hipLaunchKernelGGL((fa_fwd_fp8_kernel<D, NW>), dim3(grid), dim3(64 * NW), 0, s, p);
+                    resident_workgroups(fa_fwd_fp8_kernel<D, NW, TILED>, 64 * NW, resident));
+  hipLaunchKernelGGL((fa_fwd_fp8_kernel<D, NW, TILED>), dim3(grid), dim3(64 * NW), 0, s, p);
 }
 
-}  // namespace
-
-extern "C" int fa_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale,
-                          const float* k_descale, const float* v_descale, void* o, float* lse,
-                          int B, int H, int N, int d, float scale, int mask_kind,
-                          const int32_t* kv_lens, void* stream) {
+// Shared by fa_fwd_fp8 (one scale per head) and fa_fwd_fp8_tiled.
+int fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale,
+            const float* k_descale, const float* v_descale, void* o, float* lse, int B, int H,
+            int N, int d, float scale, int mask_kind, const int32_t* kv_lens, void* stream,
+            bool tiled) {
   if (!q || !k || !v || !q_descale || !k_descale || !v_descale || !o || !lse)
     return FA_ERR_INVALID_ARG;
   const uintptr_t al = (uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse;
@@ -375,14 +385,42 @@ extern "C" int fa_fwd_fp8(const void* q, const void* k, const void* v, const flo
   p.ascale = fabsf(scale) < kMinScale ? kMinScale : fabsf(scale);
   p.qsign = (signbit(scale) && scale != 0.f) ? 0x80808080u : 0u;
   p.causal = causal ? 1 : 0;
+  p.hg = 4;
+  p.nqt = (N + FA_FP8_TILE - 1) / FA_FP8_TILE;
   hipStream_t s = (hipStream_t)stream;
   const unsigned grid = (unsigned)(B * H * p.nqb);
-  if (d == 128) {
-    if (big) launch_fp8<128, 8>(grid, s, p);
-    else launch_fp8<128, 4>(grid, s, p);
-  } else {
-    if (big) launch_fp8<64, 8>(grid, s, p);
-    else launch_fp8<64, 4>(grid, s, p);
+#define FA_FP8_LAUNCH(T)                                     \
+  if (d == 128) {                                            \
+    if (big) launch_fp8<128, 8, T>(grid, s, p);             \
+    else launch_fp8<128, 4, T>(grid, s, p);                 \
+  } else {                                                   \
+    if (big) launch_fp8<64, 8, T>(grid, s, p);              \
+    else launch_fp8<64, 4, T>(grid, s, p);                  \
   }
+  if (tiled) {
+    FA_FP8_LAUNCH(true)
+  } else {
+    FA_FP8_LAUNCH(false)
+  }
+#undef FA_FP8_LAUNCH
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int fa_fwd_fp8(const void* q, const void* k, const void* v, const float* q_descale,
+                          const float* k_descale, const float* v_descale, void* o, float* lse,
+                          int B, int H, int N, int d, float scale, int mask_kind,
+                          const int32_t* kv_lens, void* stream) {
+  return fwd_fp8(q, k, v, q_descale, k_descale, v_descale, o, lse, B, H, N, d, scale, mask_kind,
+                 kv_lens, stream, false);
+}
+
+extern "C" int fa_fwd_fp8_tiled(const void* q, const void* k, const void* v,
+                                const float* q_descale, const float* k_descale,
+                                const float* v_descale, void* o, float* lse, int B, int H, int N,
+                                int d, float scale, int mask_kind, const int32_t* kv_lens,
+                                void* stream) {
+  return fwd_fp8(q, k, v, q_descale, k_descale, v_descale, o, lse, B, H, N, d, scale, mask_kind,
+                 kv_lens, stream, true);
 }

@@ -251,6 +251,35 @@ def dequant_fp8_f64(codes: np.ndarray, descale: np.ndarray) -> np.ndarray:
     return fp8_e4m3_to_f64(codes) * np.asarray(descale, dtype=np.float64)[:, :, None, None]
 
 
+FP8_TILE = 128   # rows per scale tile of the tiled fp8 entry point
+
+
+def _tile_rows(descale: np.ndarray, N: int, tile: int) -> np.ndarray:
+    """Per-row scale [B, H, N] from per-tile scales [B, H, ceil(N / tile)]."""
+    return np.repeat(np.asarray(descale), tile, axis=2)[:, :, :N]
+
+
+def quantize_fp8_per_tile(x: np.ndarray, tile: int = FP8_TILE):
+    """E4M3 quantization of float32 [B, H, N, d] with one scale per ``tile``
+    consecutive rows of each (batch, head): returns (codes uint8 [B, H, N, d],
+    descale float32 [B, H, ceil(N / tile)])."""
+    B, H, N, d = x.shape
+    T = -(-N // tile)
+    padded = np.zeros((B, H, T * tile, d), dtype=np.float32)
+    padded[:, :, :N] = x
+    amax = np.abs(padded.reshape(B, H, T, tile * d)).max(axis=3).astype(np.float32)
+    descale = np.where(amax > 0, amax / np.float32(FP8_MAX), np.float32(1.0)).astype(np.float32)
+    rows = _tile_rows(descale, N, tile).astype(np.float64)
+    return f32_to_fp8_e4m3(x.astype(np.float64) / rows[..., None]), descale
+
+
+def dequant_fp8_tiled_f64(codes: np.ndarray, descale: np.ndarray,
+                          tile: int = FP8_TILE) -> np.ndarray:
+    """Exact float64 values code_value * descale of per-tile quantized data."""
+    rows = _tile_rows(np.asarray(descale, dtype=np.float64), codes.shape[2], tile)
+    return fp8_e4m3_to_f64(codes) * rows[..., None]
+
+
 def _streams(seed: int, n: int = 4):
     return [np.random.Generator(np.random.PCG64(s))
             for s in np.random.SeedSequence(seed).spawn(n)]
@@ -284,6 +313,35 @@ def make_raw(B: int, H: int, N: int, d: int, dtype: str, seed: int,
         return {"q": q, "k": k, "v": v, "kv_lens": kv_lens,
                 "q_descale": qs, "k_descale": ks, "v_descale": vs}
     return {"q": q, "k": k, "v": v, "kv_lens": kv_lens}
+
+
+def make_raw_fp8_tiled(B: int, H: int, N: int, d: int, seed: int, q_mult: float = 1.0,
+                      kv_len_range: Optional[Tuple[int, int]] = None, tile_gain: float = 0.0):
+    """The draws of ``make_raw`` with Q and K quantized per FP8_TILE-row tile
+    (descales [B, H, ceil(N / FP8_TILE)]) and V per head.  With ``tile_gain``
+    > 0 every row tile of Q and of K is first multiplied by 2^u, u uniform in
+    [-tile_gain, tile_gain] (its own stream), so the tiles span different
+    ranges -- the case block quantization is for."""
+    gq, gk, gv, gl, gg = _streams(seed, 5)
+    shape = (B, H, N, d)
+    q = gq.standard_normal(shape, dtype=np.float32)
+    if q_mult != 1.0:
+        q *= np.float32(q_mult)
+    k = gk.standard_normal(shape, dtype=np.float32)
+    v = gv.standard_normal(shape, dtype=np.float32)
+    kv_lens = None
+    if kv_len_range is not None:
+        lo, hi = kv_len_range
+        kv_lens = gl.integers(lo, hi, size=B, endpoint=True).astype(np.int32)
+    T = -(-N // FP8_TILE)
+    if tile_gain > 0:
+        for t in (q, k):
+            u = gg.uniform(-tile_gain, tile_gain, size=(B, H, T))
+            t *= _tile_rows(np.exp2(u), N, FP8_TILE)[..., None].astype(np.float32)
+    (qc, qs), (kc, ks) = quantize_fp8_per_tile(q), quantize_fp8_per_tile(k)
+    vc, vs = quantize_fp8_per_head(v)
+    return {"q": qc, "k": kc, "v": vc, "kv_lens": kv_lens, "q_descale": qs, "k_descale": ks,
+            "v_descale": vs, "fp8_tiled": True, "q_f32": q, "k_f32": k, "v_f32": v}
 
 
 def make_packed(lens_q, lens_k, H: int, d: int, seed: int, q_mult: float = 1.0):
@@ -367,6 +425,10 @@ def make_bwd_inputs(wl: Workload):
 
 def inputs_f64(x: dict):
     """Exact float64 Q, K, V of a generated input dict (any dtype)."""
+    if x["q"].dtype == np.uint8 and x.get("fp8_tiled"):
+        return (dequant_fp8_tiled_f64(x["q"], x["q_descale"]),
+                dequant_fp8_tiled_f64(x["k"], x["k_descale"]),
+                dequant_fp8_f64(x["v"], x["v_descale"]))
     if x["q"].dtype == np.uint8:
         return tuple(dequant_fp8_f64(x[n], x[n + "_descale"]) for n in "qkv")
     return tuple(to_f64(x[n]) for n in "qkv")

@@ -176,6 +176,29 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, const float* q_desca
                int B, int H, int N, int d, float scale, int mask_kind,
                const int32_t* kv_lens, void* stream);
 
+/* Rows per scale tile of fa_fwd_fp8_tiled. */
+#define FA_FP8_TILE 128
+
+/* FP8 forward with block quantization at tile granularity (the youngju.dev
+ * walkthrough §9.2, "block quantization": an independent scale per block to
+ * keep the dynamic range; "FlashAttention 完整解析" §5.5, scaling per tile
+ * before the softmax): as fa_fwd_fp8, except that Q and K carry one float32
+ * scale per FA_FP8_TILE consecutive rows of each head, so the values are
+ * q_code[b,h,r,:] * q_descale[(b*H + h)*T + r/FA_FP8_TILE] and likewise for
+ * k, with T = ceil(N / FA_FP8_TILE).  Each (query tile, key tile) block of
+ * the logits is a product of E4M3 codes times q_scale * k_scale * scale,
+ * applied to the fp32 MFMA result before the softmax.  V keeps one scale per
+ * (batch, head): v_descale[b*H + h].
+ *  - q_descale, k_descale: DEVICE pointers to float32 [B * H * T];
+ *    v_descale: float32 [B * H]; 4-byte aligned, finite and positive (not
+ *    checked on the host).
+ *  - Everything else (layouts, masks, bounds, precision, errors) as for
+ *    fa_fwd_fp8. */
+int fa_fwd_fp8_tiled(const void* q, const void* k, const void* v, const float* q_descale,
+                     const float* k_descale, const float* v_descale, void* o, float* lse,
+                     int B, int H, int N, int d, float scale, int mask_kind,
+                     const int32_t* kv_lens, void* stream);
+
 /* Decode over a paged KV cache ("FlashAttention 完整解析" §7, PageAttention's
  * block table): for each request b and head h, the one query vector
  * q[b, h, :] attends to the request's n_b = seq_lens[b] cached tokens,

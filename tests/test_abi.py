@@ -28,7 +28,8 @@ def lib():
 def test_header_declares_the_entry_points():
     assert _declared() == ["fa_bwd", "fa_decode_paged", "fa_decode_paged_noalloc",
                            "fa_decode_paged_workspace_bytes", "fa_fwd", "fa_fwd_f32",
-                           "fa_fwd_fp8", "fa_fwd_general", "fa_fwd_varlen", "fa_strerror"]
+                           "fa_fwd_fp8", "fa_fwd_fp8_tiled", "fa_fwd_general", "fa_fwd_varlen",
+                           "fa_strerror"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -103,15 +104,16 @@ def test_backward_invalid_arguments_are_rejected_before_launch(lib):
     assert _bwd(lib, d=32) == fa.FA_ERR_UNSUPPORTED
 
 
-def test_fp8_invalid_arguments_are_rejected_before_launch(lib):
+@pytest.mark.parametrize("entry", ["fa_fwd_fp8", "fa_fwd_fp8_tiled"])
+def test_fp8_invalid_arguments_are_rejected_before_launch(lib, entry):
     import exact_attention_92_amd as fa
     bad = fa.FA_ERR_INVALID_ARG
     good = [0x1000 * (i + 1) for i in range(8)]
 
     def call(ptrs=good, B=1, H=1, N=16, d=64, scale=0.125, mask=0, kv=None):
-        return lib.fa_fwd_fp8(*[ctypes.c_void_p(p) if p is not None else None for p in ptrs],
-                              B, H, N, d, ctypes.c_float(scale), mask,
-                              ctypes.c_void_p(kv) if kv else None, None)
+        return getattr(lib, entry)(*[ctypes.c_void_p(p) if p is not None else None for p in ptrs],
+                                   B, H, N, d, ctypes.c_float(scale), mask,
+                                   ctypes.c_void_p(kv) if kv else None, None)
     for i in range(8):
         p = list(good)
         p[i] = None

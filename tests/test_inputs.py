@@ -115,3 +115,35 @@ def test_fp8_per_head_quantization_recipe():
         scale = ds[:, :, None, None].astype(np.float64)
         assert np.all(err <= np.maximum(2.0 ** -4 * np.abs(ref[name]), 2.0 ** -10 * scale) * 1.0001)
     assert wl.dtype == "fp8" and make_inputs(wl)["q"].dtype == np.uint8
+
+
+def test_fp8_per_tile_quantization_recipe():
+    """One E4M3 scale per 128 rows: each tile uses its full range (its largest
+    code is 448), each element is within the E4M3 rounding bound of its draw,
+    and with a single tile the recipe is the per-head one (same codes and
+    scale)."""
+    from fa_inputs import (FP8_TILE, inputs_f64, make_raw, make_raw_fp8_tiled,
+                           quantize_fp8_per_head, quantize_fp8_per_tile)
+    x = make_raw_fp8_tiled(2, 3, 300, 64, seed=5, q_mult=2.0, tile_gain=4.0)
+    q, k, v = inputs_f64(x)
+    T = -(-300 // FP8_TILE)
+    for name, deq in (("q", q), ("k", k)):
+        ds, raw = x[name + "_descale"], x[name + "_f32"]
+        assert ds.shape == (2, 3, T) and ds.dtype == np.float32
+        for t in range(T):
+            rows = slice(t * FP8_TILE, min(300, (t + 1) * FP8_TILE))
+            amax = np.abs(raw[:, :, rows]).max(axis=(2, 3))
+            assert np.allclose(ds[:, :, t], amax / 448.0, rtol=1e-7)
+            assert np.all((x[name][:, :, rows] & 0x7F).reshape(2, 3, -1).max(axis=2) == 0x7E)
+            err = np.abs(deq[:, :, rows] - raw[:, :, rows])
+            step = ds[:, :, t][:, :, None, None].astype(np.float64)
+            assert np.all(err <= np.maximum(2.0 ** -4 * np.abs(raw[:, :, rows]),
+                                            2.0 ** -10 * step) * 1.0001)
+    # the gains really spread the tiles' ranges
+    assert np.log2(x["q_descale"].max() / x["q_descale"].min()) > 4
+    assert x["v_descale"].shape == (2, 3)
+    # one tile: identical to per-head quantization
+    y = make_raw(1, 2, 100, 32, "f32", seed=9)["q"]
+    ct, st = quantize_fp8_per_tile(y)
+    ch, sh = quantize_fp8_per_head(y)
+    assert np.array_equal(ct, ch) and np.array_equal(st[:, :, 0], sh)
