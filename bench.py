@@ -56,6 +56,8 @@ def fwd_kernel_name(wl, general):
         return "fa_fwd_d128_kernel"
     name = {"bf16": "fa_fwd_bf16_kernel", "f32": "fa_fwd_f32_kernel",
             "fp8": "fa_fwd_fp8_kernel"}[wl.dtype]
+    if wl.tile_gain is not None:
+        name += " (per-tile scales)"
     return name + (" (general layout)" if general else "")
 
 
@@ -331,9 +333,10 @@ def main():
     elif wl.dtype == "fp8":
         qs, ks, vs = (up(x[n + "_descale"]) for n in "qkv")
 
+        fp8_fn = fa.fa_fwd_fp8_tiled if x.get("fp8_tiled") else fa.fa_fwd_fp8
+
         def step():
-            fa.fa_fwd_fp8(q, k, v, qs, ks, vs, o, lse, wl.scale, wl.mask_kind, kv,
-                          stream.cuda_stream)
+            fp8_fn(q, k, v, qs, ks, vs, o, lse, wl.scale, wl.mask_kind, kv, stream.cuda_stream)
     else:
         fn = fa.fa_fwd if wl.dtype == "bf16" else fa.fa_fwd_f32
 

@@ -66,6 +66,7 @@ class Workload:
     layout: str = "bhnd"       # "bnhd": tensors stored [B, N, H, d] (general forward only);
     #                            "varlen": B packed sequences, lengths U[len_range] (N = max)
     len_range: Optional[Tuple[int, int]] = None
+    tile_gain: Optional[float] = None   # fp8 only: quantize Q, K per 128-row tile (make_raw_fp8_tiled)
 
     @property
     def scale(self) -> float:
@@ -125,6 +126,11 @@ FP8_WORKLOADS = {
     "fp8_b2h32_n4096_d128_causal": Workload(
         "fp8_b2h32_n4096_d128_causal", 2, 32, 4096, 128, "fp8", MASK_CAUSAL, seed=3,
         q_mult=2.0, note="fp8 E4M3 Q, K, V with per-head scales; causal"),
+    "fp8_tiled_b2h32_n4096_d128_causal": Workload(
+        "fp8_tiled_b2h32_n4096_d128_causal", 2, 32, 4096, 128, "fp8", MASK_CAUSAL, seed=3,
+        q_mult=2.0, tile_gain=3.0,
+        note="fp8 E4M3 Q, K with one scale per 128 rows (tile ranges spread over 2^[-3, 3]), "
+             "V per head; causal"),
 }
 
 @dataclass(frozen=True)
@@ -412,6 +418,9 @@ def make_inputs(wl: Workload):
     if wl.layout == "varlen":
         n = packed_lengths(wl)
         return make_packed(n, n, wl.H, wl.d, wl.seed, q_mult=wl.q_mult)
+    if wl.tile_gain is not None:
+        return make_raw_fp8_tiled(wl.B, wl.H, wl.N, wl.d, wl.seed, q_mult=wl.q_mult,
+                                  kv_len_range=wl.kv_len_range, tile_gain=wl.tile_gain)
     return make_raw(wl.B, wl.H, wl.N, wl.d, wl.dtype, wl.seed,
                     q_mult=wl.q_mult, kv_len_range=wl.kv_len_range)
 
