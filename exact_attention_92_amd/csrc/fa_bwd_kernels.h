@@ -289,143 +289,73 @@ void fa_bwd_dq_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: one workgroup = 4 waves x 32 keys of one (batch, head)
+// dK, dV: one workgroup = 128 keys of one (batch, head), 8 waves
 // ---------------------------------------------------------------------------
-constexpr int kKvWaves = 4;
+// Waves g and g + 4 own keys k0 + 32g .. k0 + 32g + 31 and share a SIMD.  The
+// first (role A) keeps those keys' K rows in registers, rebuilds P for each
+// block of 64 query rows and accumulates dV^T += dO^T P; it hands P, rounded
+// to bf16 in the layout of an MFMA operand, to the second through LDS.  The
+// second (role B) keeps the V rows, computes dP = dO V^T, forms dS = P (dP - D)
+// and accumulates dK^T += Q^T dS.  Role B works one query block behind role
+// A, so a single barrier per block orders both the hand-over of P and the
+// staging: LDS holds three stages of a query block (Q, dO, LSE, D; block i+1
+// is written while role A reads block i and role B block i-1) and two P
+// slots per key group.
+//
+// Q and dO are stored once, row-major with rows padded to 2d + 16 bytes.
+// The operands of S = Q K^T and dP = dO V^T are 16-byte row reads; those of
+// dV^T and dK^T (Q^T, dO^T) come from the same rows through the transposing
+// LDS read (ds_read_b64_tr_b16).  Query rows are permuted within each
+// 32-row tile so that both kinds of read hit 64 distinct banks: MFMA row i
+// of S reads query pi(i) = 4(i%4) + 16(i/16) + 2((i/8)%2) + (i/4)%2, which
+// puts query 4(r%4) + 16(r/8) + 2((r/4)%2) + h in accumulator register r of
+// lane half h.  Contraction slot j (0..7) of 16-query chunk c of a tile is
+// register 4c + j%4 + 8(j/4), i.e. query 4(j%4) + 16(j/4) + 2c + h: each
+// transposing read covers 4 queries 4 rows apart, whose 64-byte pieces lie
+// 64 bytes apart in the banks.
+constexpr int kKvGroups = 4;
+constexpr int kKvThreads = 128 * kKvGroups;
 
-// Global -> register staging of one block of BQ query rows for the dK/dV
-// kernel: pieces of 4 rows x 8 dims of Q (sign-flipped when scale < 0) and
-// dO, plus LSE (log2 units) or D for one row per thread of the first 2 BQ.
-struct KvStage {
-  rsrc_t rq, rdo;
-  rsrc_t rl, rd;      // this head's LSE and D rows (N floats each)
-  uint32_t u_off;     // byte offset of this thread's piece within a block
-  unsigned qsign;
-  int N, tid;
-  bool unit;          // this thread stages a Q/dO piece
+template <int D>
+struct KvLds {
+  static constexpr int BQ = 64;                         // query rows per block
+  static constexpr uint32_t ROWB = D * 2;               // bytes per row in memory
+  static constexpr uint32_t LROW = ROWB + 16;           // bytes per row in LDS
+  static constexpr uint32_t TILE = BQ * LROW;
+  static constexpr uint32_t DO = TILE;                  // offsets within a stage
+  static constexpr uint32_t L = 2 * TILE;               // LSE, log2 units
+  static constexpr uint32_t DV = 2 * TILE + 4 * BQ;     // D
+  static constexpr uint32_t STAGE = 2 * TILE + 8 * BQ;
+  static constexpr uint32_t PSLOT = 64 * 16 * (BQ / 16);  // one wave's P chunks
+  static constexpr uint32_t P = 3 * STAGE;
+  static constexpr uint32_t BYTES = 3 * STAGE + 2 * kKvGroups * PSLOT;
+  static constexpr int CPR = D / 8;                     // 16-byte chunks per row
+  static constexpr int NCH = BQ * CPR / kKvThreads;     // chunks per thread per tensor
+  static_assert(NCH * kKvThreads == BQ * CPR, "staging shape");
 };
 
-// Branch-free: threads with nothing to load use an offset past the end of
-// the buffer range (2^31 is beyond any accepted size), which reads zeros.
-template <int D, int BQ>
-__device__ __forceinline__ void kv_stage_load(const KvStage& g, int i, u32x4_t (&qreg)[4],
-                                              u32x4_t (&dreg)[4], float& sreg) {
-  constexpr uint32_t ROWB = D * 2;
-  constexpr uint32_t kOut = 0x80000000u;
-  const uint32_t off = g.unit ? (uint32_t)(i * BQ) * ROWB + g.u_off : kOut;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    qreg[t] = buf_load16(g.rq, off + t * ROWB) ^ g.qsign;
-    dreg[t] = buf_load16(g.rdo, off + t * ROWB);
-  }
-  const int row = i * BQ + (g.tid % BQ);
-  const bool ok = row < g.N;
-  const float l = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-      g.rl, (ok && g.tid < BQ) ? 4u * row : kOut, 0, 0));
-  const float d = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-      g.rd, (ok && g.tid >= BQ && g.tid < 2 * BQ) ? 4u * row : kOut, 0, 0));
-  sreg = g.tid < BQ ? lse_log2(l, ok) : d;
-}
-
-// One block of BQ query rows for one wave's 32 keys: S = Q K^T and
-// dP = dO V^T (one key per lane, query rows permuted so register r of tile qt
-// holds query q0 + 32qt + 16(r/8) + 8hf + r%8), P = 2^(s c - LSE2),
-// dS = P (dP - D), then dV^T += dO^T P and dK^T += Q^T dS.  EDGE: the block
-// holds hidden pairs (key past kv_len, or causal key after query); the other
-// blocks skip the mask.  The next block's global loads are issued after the
-// softmax, when the scores no longer occupy registers.  The body is one
-// straight-line region (the staging loads are branch-free).
-template <int D, int BQ, bool EDGE>
-__device__ __forceinline__ void kv_block(
-    const uint16_t (*q_rows)[D + 8], const uint16_t (*do_rows)[D + 8],
-    const uint16_t (*q_cols)[BQ + 8], const uint16_t (*do_cols)[BQ + 8], const float* l_vec,
-    const float* d_vec, const u32x4_t (&kr)[D / 16], const u32x4_t (&vr)[D / 16],
-    f32x16_t (&dva)[D / 32], f32x16_t (&dka)[D / 32], const KvStage& g, int inext,
-    u32x4_t (&qreg)[4], u32x4_t (&dreg)[4], float& sreg, int q0, int key, int n_vis,
-    bool causal, float c, int n, int hf, int qperm) {
-  constexpr int KS = D / 16, DT = D / 32, QT = BQ / 32, PC = BQ / 16;
-  f32x16_t s[QT], dp[QT];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    s[qt] = zero16();
-    dp[qt] = zero16();
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const u32x4_t a = *(const u32x4_t*)&q_rows[32 * qt + qperm][16 * ks + 8 * hf];
-      s[qt] = mfma_bf16(a, kr[ks], s[qt]);
-      const u32x4_t a2 = *(const u32x4_t*)&do_rows[32 * qt + qperm][16 * ks + 8 * hf];
-      dp[qt] = mfma_bf16(a2, vr[ks], dp[qt]);
-    }
-  }
-  if constexpr (EDGE) {
-    const bool hidden_key = key >= n_vis;
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qi = q0 + 32 * qt + 16 * (r >> 3) + 8 * hf + (r & 7);
-        if (hidden_key || (causal && key > qi)) s[qt][r] = -INFINITY;
-      }
-  }
-  // Chunk pc of 16 queries = registers 8(pc%2).. of tile pc/2.
-  u32x4_t pb[PC], dsb[PC];
-#pragma unroll
-  for (int pc = 0; pc < PC; ++pc) {
-    const int qt = pc >> 1, r0 = 8 * (pc & 1);
-    const float4* lp = (const float4*)&l_vec[16 * pc + 8 * hf];
-    const float4* dpp = (const float4*)&d_vec[16 * pc + 8 * hf];
-    const float4 la = lp[0], lb = lp[1], da = dpp[0], db = dpp[1];
-    const float lv[8] = {la.x, la.y, la.z, la.w, lb.x, lb.y, lb.z, lb.w};
-    const float dv[8] = {da.x, da.y, da.z, da.w, db.x, db.y, db.z, db.w};
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qt][r0 + 2 * w], c, -lv[2 * w]));
-      const float p1 =
-          __builtin_amdgcn_exp2f(__builtin_fmaf(s[qt][r0 + 2 * w + 1], c, -lv[2 * w + 1]));
-      pb[pc][w] = pack_bf16(p0, p1);
-      dsb[pc][w] = pack_bf16(p0 * (dp[qt][r0 + 2 * w] - dv[2 * w]),
-                             p1 * (dp[qt][r0 + 2 * w + 1] - dv[2 * w + 1]));
-    }
-  }
-  // Past the last block the loads read zeros and rows past N; unused.
-  kv_stage_load<D, BQ>(g, inext, qreg, dreg, sreg);
-  // A operands: rows 32dt + n of the transposed tiles, queries 16pc + 8hf + 0..7.
-#pragma unroll
-  for (int pc = 0; pc < PC; ++pc)
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const u32x4_t a = *(const u32x4_t*)&do_cols[32 * dt + n][16 * pc + 8 * hf];
-      dva[dt] = mfma_bf16(a, pb[pc], dva[dt]);
-      const u32x4_t a2 = *(const u32x4_t*)&q_cols[32 * dt + n][16 * pc + 8 * hf];
-      dka[dt] = mfma_bf16(a2, dsb[pc], dka[dt]);
-    }
+// Query (within a 32-row tile) of accumulator register r of lane half h.
+__device__ __forceinline__ int kv_query(int r, int h) {
+  return 4 * (r & 3) + 16 * (r >> 3) + 2 * ((r >> 2) & 1) + h;
 }
 
 template <int D>
-__global__ __launch_bounds__(64 * kKvWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dkdv_kernel(BwdParams p) {
-  constexpr int kThreads = 64 * kKvWaves;
-  constexpr int BK = 32 * kKvWaves;  // keys per workgroup
-  constexpr int BQ = 64;             // query rows per block
-  constexpr int KS = D / 16;         // k-steps over d
-  constexpr int DT = D / 32;         // 32-row tiles of dK^T, dV^T
-  constexpr int RLD = D + 8;
-  constexpr int TLD = BQ + 8;
-  constexpr uint32_t ROWB = D * 2;
-  constexpr int CPR = D / 8;
-  constexpr int UNITS = (BQ / 4) * CPR;
-  static_assert(UNITS <= kThreads && 2 * BQ <= kThreads, "staging shape");
+  using Ly = KvLds<D>;
+  constexpr int BQ = Ly::BQ;
+  constexpr int BK = 32 * kKvGroups;  // keys per workgroup
+  constexpr int KS = D / 16;          // k-steps over d
+  constexpr int DT = D / 32;          // 32-row tiles of dK^T, dV^T
+  constexpr uint32_t ROWB = Ly::ROWB, LROW = Ly::LROW;
 
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[2][BQ][RLD];
-  __shared__ __attribute__((aligned(16))) uint16_t do_lds[2][BQ][RLD];
-  __shared__ __attribute__((aligned(16))) uint16_t qt_lds[2][D][TLD];
-  __shared__ __attribute__((aligned(16))) uint16_t dot_lds[2][D][TLD];
-  __shared__ __attribute__((aligned(16))) float l_lds[2][BQ];   // LSE, log2 units
-  __shared__ __attribute__((aligned(16))) float d_lds[2][BQ];   // D
+  __shared__ __attribute__((aligned(16))) uint8_t lds[Ly::BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave & (kKvGroups - 1);
+  const bool role_b = wave >= kKvGroups;
   const int n = lane & 31;
   const int hf = lane >> 5;
   const bool causal = p.causal != 0;
@@ -437,7 +367,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   const size_t hoff = (size_t)bh * (size_t)N * D;
   const int n_vis = visible_len(p, b);
   const int k0 = kb * BK;
-  const int kw0 = k0 + wave * 32;
+  const int kw0 = k0 + grp * 32;
   const int key = kw0 + n;
   uint16_t* dKh = (uint16_t*)p.dk + hoff;
   uint16_t* dVh = (uint16_t*)p.dv + hoff;
@@ -446,119 +376,231 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     // No query sees these keys: their gradients are 0.
     const int rows = min(BK, N - k0);
     const u32x4_t z = {0u, 0u, 0u, 0u};
-    for (int i = tid; i < rows * CPR; i += kThreads) {
-      const size_t off = (size_t)(k0 + i / CPR) * D + 8 * (i % CPR);
+    for (int i = tid; i < rows * Ly::CPR; i += kKvThreads) {
+      const size_t off = (size_t)(k0 + i / Ly::CPR) * D + 8 * (i % Ly::CPR);
       *(u32x4_t*)(dKh + off) = z;
       *(u32x4_t*)(dVh + off) = z;
     }
     return;
   }
 
-  // This lane's key: K and V rows in the B-operand layout of S = Q K^T and
-  // dP = dO V^T.  Keys at or past kv_len read as zero.
-  u32x4_t kr[KS], vr[KS];
+  // This lane's key: its K row (role A) or V row (role B) in the B-operand
+  // layout of S = Q K^T / dP = dO V^T.  Keys at or past kv_len read as zero.
+  u32x4_t kv[KS];
   {
     const uint32_t bytes = (uint32_t)n_vis * ROWB;
-    const rsrc_t rk = make_rsrc((const uint16_t*)p.k + hoff, bytes);
-    const rsrc_t rv = make_rsrc((const uint16_t*)p.v + hoff, bytes);
+    const rsrc_t r = make_rsrc((const uint16_t*)(role_b ? p.v : p.k) + hoff, bytes);
     const uint32_t off = (uint32_t)key * ROWB + 16u * hf;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      kr[ks] = buf_load16(rk, off + 32u * ks);
-      vr[ks] = buf_load16(rv, off + 32u * ks);
-    }
+    for (int ks = 0; ks < KS; ++ks) kv[ks] = buf_load16(r, off + 32u * ks);
   }
+
+  // Staging of a query block: NCH 16-byte chunks of Q (sign-flipped when
+  // scale < 0) and of dO per thread, and one LSE (threads 0..63) or D value
+  // (64..127), stored at the position its consumers read: position
+  // 32t + 16h + r holds query 32t + kv_query(r, h).
+  const rsrc_t rq = make_rsrc((const uint16_t*)p.q + hoff, (uint32_t)N * ROWB);
+  const rsrc_t rdo = make_rsrc((const uint16_t*)p.dout + hoff, (uint32_t)N * ROWB);
+  const rsrc_t rl = make_rsrc(p.lse + (size_t)bh * N, (uint32_t)N * 4u);
+  const rsrc_t rd = make_rsrc(p.dps + (size_t)bh * N, (uint32_t)N * 4u);
+  uint32_t g_off[Ly::NCH], l_off[Ly::NCH];
+#pragma unroll
+  for (int u = 0; u < Ly::NCH; ++u) {
+    const int id = tid + kKvThreads * u, row = id / Ly::CPR, ch = id % Ly::CPR;
+    g_off[u] = (uint32_t)row * ROWB + 16u * ch;
+    l_off[u] = (uint32_t)row * LROW + 16u * ch;
+  }
+  const int spos = tid & (BQ - 1);
+  const int sq = 32 * (spos >> 5) + kv_query(spos & 15, (spos >> 4) & 1);
+  const bool s_lse = tid < BQ, s_d = tid >= BQ && tid < 2 * BQ;
+  const uint32_t s_lds = (s_lse ? Ly::L : Ly::DV) + 4u * spos;
+  u32x4_t gq[Ly::NCH], gd[Ly::NCH];
+  float gs = 0.f;
+  auto stage_load = [&](int i) {
+    const uint32_t base = (uint32_t)(i * BQ) * ROWB;
+#pragma unroll
+    for (int u = 0; u < Ly::NCH; ++u) {
+      gq[u] = buf_load16(rq, base + g_off[u]) ^ p.qsign;
+      gd[u] = buf_load16(rdo, base + g_off[u]);
+    }
+    const int row = i * BQ + sq;
+    const bool ok = row < N;
+    const uint32_t off = ok ? 4u * (uint32_t)row : 0x80000000u;
+    if (s_lse) gs = lse_log2(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, off, 0, 0)), ok);
+    else if (s_d) gs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, off, 0, 0));
+  };
+  auto stage_store = [&](uint32_t st) {
+#pragma unroll
+    for (int u = 0; u < Ly::NCH; ++u) {
+      *(u32x4_t*)(lds + st + l_off[u]) = gq[u];
+      *(u32x4_t*)(lds + st + Ly::DO + l_off[u]) = gd[u];
+    }
+    if (s_lse || s_d) *(float*)(lds + st + s_lds) = gs;
+  };
+
+  // Operand addresses (byte offsets within a stage's tile).  Row reads: MFMA
+  // row n of tile t reads query 32t + pi(n), d elements 16ks + 8hf..+7.
+  const int pin = 4 * (n & 3) + 16 * (n >> 4) + 2 * ((n >> 3) & 1) + ((n >> 2) & 1);
+  const uint32_t a_row = (uint32_t)pin * LROW + 16u * hf;
+  // Transposing reads: lane 16g + 4s + t reads query 4s + (g/2) (+ 32 tile
+  // + 16 half + 2 chunk), d columns 16(g%2) + 4t..+3 (+ 32 dt); it receives
+  // the 4 queries of d column 16(g%2) + (lane%16).
+  const int tg = lane >> 4, ts = (lane >> 2) & 3, tt = lane & 3;
+  const uint32_t a_tr = (uint32_t)(4 * ts + (tg >> 1)) * LROW + 32u * (tg & 1) + 8u * tt;
+  const uint32_t lv_off = 4u * (16 * hf);      // LSE / D of this lane's registers
+  const uint32_t p_off = Ly::P + Ly::PSLOT * (uint32_t)grp + 16u * lane;
+
+  auto rd16 = [&](uint32_t off) { return *(const u32x4_t*)(lds + off); };
+  auto rd_tr = [&](uint32_t off) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(lds + off));
+    return __builtin_bit_cast(u32x2_t, v);
+  };
+  // A operand of dV^T / dK^T for 16-query chunk c of tile t, rows 32dt..:
+  // contraction slots 0..3 from the first half of the tile, 4..7 from the
+  // second.
+  auto tr_operand = [&](uint32_t tile, int t, int c, int dt) {
+    const uint32_t o = tile + a_tr + (uint32_t)(32 * t + 2 * c) * LROW + 64u * dt;
+    const u32x2_t lo = rd_tr(o), hi = rd_tr(o + 16 * LROW);
+    const u32x4_t a = {lo[0], lo[1], hi[0], hi[1]};
+    return a;
+  };
+
+  f32x16_t acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16();
+  const float c = p.c;
 
   // Query blocks: causal -> from the block holding query k0 on; else all.
   const int qb0 = causal ? k0 / BQ : 0;
   const int nqb = (N + BQ - 1) / BQ;
+  const int nblk = nqb - qb0;
 
-  // Staging of query block i: pieces of 4 rows x 8 dims of Q and dO, stored
-  // row-major and transposed; LSE (log2 units) and D for its rows.
-  const bool st_unit = tid < UNITS;
-  const int rg = tid % (BQ / 4), dc = tid / (BQ / 4);
-  const uint32_t u_off = (uint32_t)(4 * rg) * ROWB + 16u * dc;
-  const rsrc_t rq = make_rsrc((const uint16_t*)p.q + hoff, (uint32_t)N * ROWB);
-  const rsrc_t rdo = make_rsrc((const uint16_t*)p.dout + hoff, (uint32_t)N * ROWB);
-  const float* Lh = p.lse + (size_t)bh * N;
-  const float* Dh = p.dps + (size_t)bh * N;
-  u32x4_t qreg[4], dreg[4];
-  float sreg = 0.f;
-  KvStage g;
-  g.rq = rq;
-  g.rdo = rdo;
-  g.rl = make_rsrc(Lh, (uint32_t)N * 4u);
-  g.rd = make_rsrc(Dh, (uint32_t)N * 4u);
-  g.u_off = u_off;
-  g.qsign = p.qsign;
-  g.N = N;
-  g.tid = tid;
-  g.unit = st_unit;
-  auto store_block = [&](int buf) {
-    if (st_unit) {
-      u32x2_t lo[4], hi[4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) *(u32x4_t*)&q_lds[buf][4 * rg + t][8 * dc] = qreg[t];
-      transpose4x8(qreg, lo, hi);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        *(u32x2_t*)&qt_lds[buf][8 * dc + 2 * w][4 * rg] = lo[w];
-        *(u32x2_t*)&qt_lds[buf][8 * dc + 2 * w + 1][4 * rg] = hi[w];
-      }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) *(u32x4_t*)&do_lds[buf][4 * rg + t][8 * dc] = dreg[t];
-      transpose4x8(dreg, lo, hi);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        *(u32x2_t*)&dot_lds[buf][8 * dc + 2 * w][4 * rg] = lo[w];
-        *(u32x2_t*)&dot_lds[buf][8 * dc + 2 * w + 1][4 * rg] = hi[w];
-      }
-    }
-    if (tid < BQ) l_lds[buf][tid] = sreg;
-    else if (tid < 2 * BQ) d_lds[buf][tid - BQ] = sreg;
-  };
-
-  f32x16_t dka[DT], dva[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    dka[dt] = zero16();
-    dva[dt] = zero16();
-  }
-  const float c = p.c;
-  const int qperm = row_perm(n);
-
-  if (qb0 < nqb) {
-    kv_stage_load<D, BQ>(g, qb0, qreg, dreg, sreg);
-    store_block(0);
-  }
+  stage_load(qb0);
+  stage_store(0);
   __syncthreads();
 
-  for (int i = qb0; i < nqb; ++i) {
-    const int buf = (i - qb0) & 1;
-    const int q0 = i * BQ;
-    // Every key of this wave is hidden, or (causal) comes after every query
-    // of the block: nothing to add, only the staging goes on.
-    const bool wave_skip = kw0 >= n_vis || (causal && q0 + BQ - 1 < kw0);
-    const bool edge = (causal && q0 < kw0 + 31) || (kw0 + 31 >= n_vis);
-    if (wave_skip)
-      kv_stage_load<D, BQ>(g, i + 1, qreg, dreg, sreg);
-    else if (edge)
-      kv_block<D, BQ, true>(q_lds[buf], do_lds[buf], qt_lds[buf], dot_lds[buf], l_lds[buf],
-                            d_lds[buf], kr, vr, dva, dka, g, i + 1, qreg, dreg, sreg, q0, key,
-                            n_vis, causal, c, n, hf, qperm);
-    else
-      kv_block<D, BQ, false>(q_lds[buf], do_lds[buf], qt_lds[buf], dot_lds[buf], l_lds[buf],
-                             d_lds[buf], kr, vr, dva, dka, g, i + 1, qreg, dreg, sreg, q0, key,
-                             n_vis, causal, c, n, hf, qperm);
-    if (i + 1 < nqb) store_block(buf ^ 1);
-    __syncthreads();
+  uint32_t s_cur = 0, s_prev = 2 * Ly::STAGE, s_next = Ly::STAGE;   // stages of i, i-1, i+1
+  for (int it = 0; it <= nblk; ++it) {
+    const bool more = it + 1 < nblk;
+    if (more) stage_load(qb0 + it + 1);
+    // Block i of this role: role A block it, role B block it - 1.
+    const int i = role_b ? it - 1 : it;
+    const int q0 = (qb0 + i) * BQ;
+    const bool active = role_b ? it > 0 : it < nblk;
+    // Every key of this group is hidden, or (causal) comes after every query
+    // of the block: nothing to add.
+    const bool skip = kw0 >= n_vis || (causal && q0 + BQ - 1 < kw0);
+    const uint32_t pslot = p_off + (uint32_t)(i & 1) * (kKvGroups * Ly::PSLOT);
+    if (active && !skip && !role_b) {
+      // S = Q K^T; P = 2^(s c - LSE2); hidden pairs (key past kv_len, or
+      // causal key after query) masked to 0 on blocks that hold any.
+      const uint32_t st = s_cur;
+      f32x16_t s[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        s[t] = zero16();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          s[t] = mfma_bf16(rd16(st + a_row + (uint32_t)(32 * t) * LROW + 32u * ks), kv[ks], s[t]);
+      }
+      if ((causal && q0 < kw0 + 31) || kw0 + 31 >= n_vis) {
+        const bool hidden_key = key >= n_vis;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (hidden_key || (causal && key > q0 + 32 * t + kv_query(r, hf))) s[t][r] = -INFINITY;
+      }
+      u32x4_t pb[4];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        float pr[16];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const float4 l4 = *(const float4*)(lds + st + Ly::L + lv_off + 4u * (32 * t + 4 * m));
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            pr[4 * m + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][4 * m + e], c, -lv[e]));
+        }
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          const int r0 = 4 * cc;
+          const u32x4_t v = {pack_bf16(pr[r0], pr[r0 + 1]), pack_bf16(pr[r0 + 2], pr[r0 + 3]),
+                             pack_bf16(pr[r0 + 8], pr[r0 + 9]),
+                             pack_bf16(pr[r0 + 10], pr[r0 + 11])};
+          pb[2 * t + cc] = v;
+        }
+      }
+#pragma unroll
+      for (int pc = 0; pc < 4; ++pc) *(u32x4_t*)(lds + pslot + 1024u * pc) = pb[pc];
+      // dV^T += dO^T P.
+#pragma unroll
+      for (int pc = 0; pc < 4; ++pc)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          acc[dt] = mfma_bf16(tr_operand(st + Ly::DO, pc >> 1, pc & 1, dt), pb[pc], acc[dt]);
+    }
+    if (active && !skip && role_b) {
+      // dP = dO V^T; dS = P (dP - D) with role A's P; dK^T += Q^T dS.
+      const uint32_t st = s_prev;
+      f32x16_t dp[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        dp[t] = zero16();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          dp[t] = mfma_bf16(rd16(st + Ly::DO + a_row + (uint32_t)(32 * t) * LROW + 32u * ks),
+                            kv[ks], dp[t]);
+      }
+      u32x4_t pb[4], dsb[4];
+#pragma unroll
+      for (int pc = 0; pc < 4; ++pc) pb[pc] = rd16(pslot + 1024u * pc);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        float dv[16];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const float4 d4 = *(const float4*)(lds + st + Ly::DV + lv_off + 4u * (32 * t + 4 * m));
+          dv[4 * m] = d4.x;
+          dv[4 * m + 1] = d4.y;
+          dv[4 * m + 2] = d4.z;
+          dv[4 * m + 3] = d4.w;
+        }
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          u32x4_t v;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const int r = 4 * cc + 2 * (w & 1) + 8 * (w >> 1);
+            const unsigned pp = pb[2 * t + cc][w];
+            const float p0 = __uint_as_float(pp << 16), p1 = __uint_as_float(pp & 0xffff0000u);
+            v[w] = pack_bf16(p0 * (dp[t][r] - dv[r]), p1 * (dp[t][r + 1] - dv[r + 1]));
+          }
+          dsb[2 * t + cc] = v;
+        }
+      }
+#pragma unroll
+      for (int pc = 0; pc < 4; ++pc)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          acc[dt] = mfma_bf16(tr_operand(st, pc >> 1, pc & 1, dt), dsb[pc], acc[dt]);
+    }
+    if (more) stage_store(s_next);
+    if (it < nblk) __syncthreads();
+    const uint32_t s_free = s_prev;
+    s_prev = s_cur;
+    s_cur = s_next;
+    s_next = s_free;
   }
 
   if (key < N) {
-    store_rows<D>(dVh + (size_t)key * D, dva, 1.f, hf);
     // Q was staged with its sign flipped when scale < 0, so |scale| restores
     // scale * dS^T Q.
-    store_rows<D>(dKh + (size_t)key * D, dka, p.ascale, hf);
+    if (role_b) store_rows<D>(dKh + (size_t)key * D, acc, p.ascale, hf);
+    else store_rows<D>(dVh + (size_t)key * D, acc, 1.f, hf);
   }
 }
 
@@ -584,12 +626,12 @@ bool launch_bwd(BwdParams p, int B, hipStream_t s) {
   if (big) launch_dq<D, 8>(gq, s, p);
   else launch_dq<D, 4>(gq, s, p);
   if (hipGetLastError() != hipSuccess) return false;
-  p.nb = (p.N + 32 * kKvWaves - 1) / (32 * kKvWaves);
+  p.nb = (p.N + 32 * kKvGroups - 1) / (32 * kKvGroups);
   const unsigned gk = (unsigned)(B * p.H * p.nb);
   static std::atomic<long long> resident_kv{0};
   p.hg = head_group(p.causal != 0, gk,
-                    resident_workgroups(fa_bwd_dkdv_kernel<D>, 64 * kKvWaves, resident_kv));
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D>), dim3(gk), dim3(64 * kKvWaves), 0, s, p);
+                    resident_workgroups(fa_bwd_dkdv_kernel<D>, kKvThreads, resident_kv));
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D>), dim3(gk), dim3(kKvThreads), 0, s, p);
   return hipGetLastError() == hipSuccess;
 }
 
