@@ -412,30 +412,32 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   }
   const int spos = tid & (BQ - 1);
   const int sq = 32 * (spos >> 5) + kv_query(spos & 15, (spos >> 4) & 1);
-  const bool s_lse = tid < BQ, s_d = tid >= BQ && tid < 2 * BQ;
-  const uint32_t s_lds = (s_lse ? Ly::L : Ly::DV) + 4u * spos;
+  const uint32_t s_lds = (wave == 0 ? Ly::L : Ly::DV) + 4u * spos;
   u32x4_t gq[Ly::NCH], gd[Ly::NCH];
   float gs = 0.f;
+  // The loads are only waited for at stage_store, at the end of the
+  // iteration that issued them (the sign flip and the LSE conversion happen
+  // there too).
+  bool gs_ok = false;
   auto stage_load = [&](int i) {
     const uint32_t base = (uint32_t)(i * BQ) * ROWB;
 #pragma unroll
     for (int u = 0; u < Ly::NCH; ++u) {
-      gq[u] = buf_load16(rq, base + g_off[u]) ^ p.qsign;
+      gq[u] = buf_load16(rq, base + g_off[u]);
       gd[u] = buf_load16(rdo, base + g_off[u]);
     }
     const int row = i * BQ + sq;
-    const bool ok = row < N;
-    const uint32_t off = ok ? 4u * (uint32_t)row : 0x80000000u;
-    if (s_lse) gs = lse_log2(__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, off, 0, 0)), ok);
-    else if (s_d) gs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, off, 0, 0));
+    gs_ok = row < N;
+    const uint32_t off = gs_ok ? 4u * (uint32_t)row : 0x80000000u;
+    if (wave < 2) gs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(wave == 0 ? rl : rd, off, 0, 0));
   };
   auto stage_store = [&](uint32_t st) {
 #pragma unroll
     for (int u = 0; u < Ly::NCH; ++u) {
-      *(u32x4_t*)(lds + st + l_off[u]) = gq[u];
+      *(u32x4_t*)(lds + st + l_off[u]) = gq[u] ^ p.qsign;
       *(u32x4_t*)(lds + st + Ly::DO + l_off[u]) = gd[u];
     }
-    if (s_lse || s_d) *(float*)(lds + st + s_lds) = gs;
+    if (wave < 2) *(float*)(lds + st + s_lds) = wave == 0 ? lse_log2(gs, gs_ok) : gs;
   };
 
   // Operand addresses (byte offsets within a stage's tile).  Row reads: MFMA
@@ -494,81 +496,80 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
     const bool skip = kw0 >= n_vis || (causal && q0 + BQ - 1 < kw0);
     const uint32_t pslot = p_off + (uint32_t)(i & 1) * (kKvGroups * Ly::PSLOT);
     if (active && !skip && !role_b) {
-      // S = Q K^T; P = 2^(s c - LSE2); hidden pairs (key past kv_len, or
-      // causal key after query) masked to 0 on blocks that hold any.
+      // S = Q K^T, P = 2^(s c - LSE2), dV^T += dO^T P, in the order tile 0
+      // of S, tile 1 of S, P of tile 0, its dV products, P of tile 1, its dV
+      // products: the exponentials of one tile run beside the MFMAs of the
+      // other.  On blocks holding hidden pairs (key past kv_len, or causal
+      // key after query) S starts from -inf there, so their P is 0.
       const uint32_t st = s_cur;
-      f32x16_t s[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        s[t] = zero16();
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          s[t] = mfma_bf16(rd16(st + a_row + (uint32_t)(32 * t) * LROW + 32u * ks), kv[ks], s[t]);
-      }
+      f32x16_t s0 = zero16(), s1 = zero16();
       if ((causal && q0 < kw0 + 31) || kw0 + 31 >= n_vis) {
-        const bool hidden_key = key >= n_vis;
+        const int thr = key >= n_vis ? (1 << 30) : (causal ? key : -1);
+        const int lim = thr - q0 - hf;   // query 32t + kv_query(r, hf) hidden iff below thr
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (hidden_key || (causal && key > q0 + 32 * t + kv_query(r, hf))) s[t][r] = -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+          s0[r] = kv_query(r, 0) < lim ? -INFINITY : 0.f;
+          s1[r] = 32 + kv_query(r, 0) < lim ? -INFINITY : 0.f;
+        }
       }
-      u32x4_t pb[4];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int ks = 0; ks < KS; ++ks) s0 = mfma_bf16(rd16(st + a_row + 32u * ks), kv[ks], s0);
+      float lv[32];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const float4 l4 = *(const float4*)(lds + st + Ly::L + lv_off + 4u * (32 * (m >> 2) + 4 * (m & 3)));
+        lv[4 * m] = l4.x;
+        lv[4 * m + 1] = l4.y;
+        lv[4 * m + 2] = l4.z;
+        lv[4 * m + 3] = l4.w;
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        s1 = mfma_bf16(rd16(st + a_row + 32u * LROW + 32u * ks), kv[ks], s1);
+      auto p_tile = [&](const f32x16_t& sv, const float* l, int t) {
         float pr[16];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const float4 l4 = *(const float4*)(lds + st + Ly::L + lv_off + 4u * (32 * t + 4 * m));
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            pr[4 * m + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][4 * m + e], c, -lv[e]));
-        }
+        for (int r = 0; r < 16; ++r)
+          pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[r], c, -l[r]));
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
           const int r0 = 4 * cc;
           const u32x4_t v = {pack_bf16(pr[r0], pr[r0 + 1]), pack_bf16(pr[r0 + 2], pr[r0 + 3]),
                              pack_bf16(pr[r0 + 8], pr[r0 + 9]),
                              pack_bf16(pr[r0 + 10], pr[r0 + 11])};
-          pb[2 * t + cc] = v;
+          *(u32x4_t*)(lds + pslot + 1024u * (2 * t + cc)) = v;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+            acc[dt] = mfma_bf16(tr_operand(st + Ly::DO, t, cc, dt), v, acc[dt]);
         }
-      }
-#pragma unroll
-      for (int pc = 0; pc < 4; ++pc) *(u32x4_t*)(lds + pslot + 1024u * pc) = pb[pc];
-      // dV^T += dO^T P.
-#pragma unroll
-      for (int pc = 0; pc < 4; ++pc)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          acc[dt] = mfma_bf16(tr_operand(st + Ly::DO, pc >> 1, pc & 1, dt), pb[pc], acc[dt]);
+      };
+      p_tile(s0, lv, 0);
+      p_tile(s1, lv + 16, 1);
     }
     if (active && !skip && role_b) {
-      // dP = dO V^T; dS = P (dP - D) with role A's P; dK^T += Q^T dS.
+      // dP = dO V^T; dS = P (dP - D) with role A's P; dK^T += Q^T dS, in the
+      // same tile order as role A.
       const uint32_t st = s_prev;
-      f32x16_t dp[2];
+      f32x16_t d0 = zero16(), d1 = zero16();
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        dp[t] = zero16();
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          dp[t] = mfma_bf16(rd16(st + Ly::DO + a_row + (uint32_t)(32 * t) * LROW + 32u * ks),
-                            kv[ks], dp[t]);
-      }
-      u32x4_t pb[4], dsb[4];
+      for (int ks = 0; ks < KS; ++ks)
+        d0 = mfma_bf16(rd16(st + Ly::DO + a_row + 32u * ks), kv[ks], d0);
+      u32x4_t pb[4];
 #pragma unroll
       for (int pc = 0; pc < 4; ++pc) pb[pc] = rd16(pslot + 1024u * pc);
+      float dv[32];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        float dv[16];
+      for (int m = 0; m < 8; ++m) {
+        const float4 d4 = *(const float4*)(lds + st + Ly::DV + lv_off + 4u * (32 * (m >> 2) + 4 * (m & 3)));
+        dv[4 * m] = d4.x;
+        dv[4 * m + 1] = d4.y;
+        dv[4 * m + 2] = d4.z;
+        dv[4 * m + 3] = d4.w;
+      }
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const float4 d4 = *(const float4*)(lds + st + Ly::DV + lv_off + 4u * (32 * t + 4 * m));
-          dv[4 * m] = d4.x;
-          dv[4 * m + 1] = d4.y;
-          dv[4 * m + 2] = d4.z;
-          dv[4 * m + 3] = d4.w;
-        }
+      for (int ks = 0; ks < KS; ++ks)
+        d1 = mfma_bf16(rd16(st + Ly::DO + a_row + 32u * LROW + 32u * ks), kv[ks], d1);
+      auto ds_tile = [&](const f32x16_t& dpv, const float* dd, int t) {
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
           u32x4_t v;
@@ -577,16 +578,15 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
             const int r = 4 * cc + 2 * (w & 1) + 8 * (w >> 1);
             const unsigned pp = pb[2 * t + cc][w];
             const float p0 = __uint_as_float(pp << 16), p1 = __uint_as_float(pp & 0xffff0000u);
-            v[w] = pack_bf16(p0 * (dp[t][r] - dv[r]), p1 * (dp[t][r + 1] - dv[r + 1]));
+            v[w] = pack_bf16(p0 * (dpv[r] - dd[r]), p1 * (dpv[r + 1] - dd[r + 1]));
           }
-          dsb[2 * t + cc] = v;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+            acc[dt] = mfma_bf16(tr_operand(st, t, cc, dt), v, acc[dt]);
         }
-      }
-#pragma unroll
-      for (int pc = 0; pc < 4; ++pc)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          acc[dt] = mfma_bf16(tr_operand(st, pc >> 1, pc & 1, dt), dsb[pc], acc[dt]);
+      };
+      ds_tile(d0, dv, 0);
+      ds_tile(d1, dv + 16, 1);
     }
     if (more) stage_store(s_next);
     if (it < nblk) __syncthreads();
