@@ -324,7 +324,7 @@ struct KvLds {
   static constexpr uint32_t TILE = BQ * LROW;
   static constexpr uint32_t DO = TILE;                  // offsets within a stage
   static constexpr uint32_t L = 2 * TILE;               // LSE, log2 units
-  static constexpr uint32_t DV = 2 * TILE + 4 * BQ;     // D
+  static constexpr uint32_t DV = 2 * TILE + 4 * BQ;     // -D
   static constexpr uint32_t STAGE = 2 * TILE + 8 * BQ;
   static constexpr uint32_t PSLOT = 64 * 16 * (BQ / 16);  // one wave's P chunks
   static constexpr uint32_t P = 3 * STAGE;
@@ -396,7 +396,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
   }
 
   // Staging of a query block: NCH 16-byte chunks of Q (sign-flipped when
-  // scale < 0) and of dO per thread, and one LSE (threads 0..63) or D value
+  // scale < 0) and of dO per thread, and one LSE (threads 0..63) or -D value
   // (64..127), stored at the position its consumers read: position
   // 32t + 16h + r holds query 32t + kv_query(r, h).
   const rsrc_t rq = make_rsrc((const uint16_t*)p.q + hoff, (uint32_t)N * ROWB);
@@ -437,7 +437,7 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
       *(u32x4_t*)(lds + st + l_off[u]) = gq[u] ^ p.qsign;
       *(u32x4_t*)(lds + st + Ly::DO + l_off[u]) = gd[u];
     }
-    if (wave < 2) *(float*)(lds + st + s_lds) = wave == 0 ? lse_log2(gs, gs_ok) : gs;
+    if (wave < 2) *(float*)(lds + st + s_lds) = wave == 0 ? lse_log2(gs, gs_ok) : -gs;
   };
 
   // Operand addresses (byte offsets within a stage's tile).  Row reads: MFMA
@@ -550,26 +550,28 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
       // dP = dO V^T; dS = P (dP - D) with role A's P; dK^T += Q^T dS, in the
       // same tile order as role A.
       const uint32_t st = s_prev;
-      f32x16_t d0 = zero16(), d1 = zero16();
+      // The accumulators start from -D (staged negated), so they end as dP - D.
+      f32x16_t d0, d1;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const float4 d4 =
+            *(const float4*)(lds + st + Ly::DV + lv_off + 4u * (32 * (m >> 2) + 4 * (m & 3)));
+        f32x16_t& dd = m < 4 ? d0 : d1;
+        dd[4 * (m & 3)] = d4.x;
+        dd[4 * (m & 3) + 1] = d4.y;
+        dd[4 * (m & 3) + 2] = d4.z;
+        dd[4 * (m & 3) + 3] = d4.w;
+      }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         d0 = mfma_bf16(rd16(st + Ly::DO + a_row + 32u * ks), kv[ks], d0);
       u32x4_t pb[4];
 #pragma unroll
       for (int pc = 0; pc < 4; ++pc) pb[pc] = rd16(pslot + 1024u * pc);
-      float dv[32];
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const float4 d4 = *(const float4*)(lds + st + Ly::DV + lv_off + 4u * (32 * (m >> 2) + 4 * (m & 3)));
-        dv[4 * m] = d4.x;
-        dv[4 * m + 1] = d4.y;
-        dv[4 * m + 2] = d4.z;
-        dv[4 * m + 3] = d4.w;
-      }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         d1 = mfma_bf16(rd16(st + Ly::DO + a_row + 32u * LROW + 32u * ks), kv[ks], d1);
-      auto ds_tile = [&](const f32x16_t& dpv, const float* dd, int t) {
+      auto ds_tile = [&](const f32x16_t& dpv, int t) {
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
           u32x4_t v;
@@ -578,15 +580,15 @@ void fa_bwd_dkdv_kernel(BwdParams p) {
             const int r = 4 * cc + 2 * (w & 1) + 8 * (w >> 1);
             const unsigned pp = pb[2 * t + cc][w];
             const float p0 = __uint_as_float(pp << 16), p1 = __uint_as_float(pp & 0xffff0000u);
-            v[w] = pack_bf16(p0 * (dpv[r] - dd[r]), p1 * (dpv[r + 1] - dd[r + 1]));
+            v[w] = pack_bf16(p0 * dpv[r], p1 * dpv[r + 1]);
           }
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt)
             acc[dt] = mfma_bf16(tr_operand(st, t, cc, dt), v, acc[dt]);
         }
       };
-      ds_tile(d0, dv, 0);
-      ds_tile(d1, dv + 16, 1);
+      ds_tile(d0, 0);
+      ds_tile(d1, 1);
     }
     if (more) stage_store(s_next);
     if (it < nblk) __syncthreads();
