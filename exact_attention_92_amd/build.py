@@ -27,11 +27,11 @@ HIPCC_FLAGS = [
 # ordinary VGPRs: left to its own choice the compiler moves the d = 256
 # kernel's accumulators into AGPRs and copies them back on every block
 # (425 -> 732 TFLOP/s at d = 256; the d <= 128 kernels never need AGPRs and
-# are unchanged).  The backward's d = 64 kernels too (8-15% faster: the dK/dV
-# kernel then needs no AGPR<->VGPR copies); its d = 128 kernels (fa_bwd.hip,
-# ~450 registers in dK/dV) are left to the compiler's default, which is 2%
-# faster there.
+# are unchanged).  The backward kernels too: bitwise-identical gradients,
+# +4-6% on causal N = 1024 (whose 4-wave dQ kernel otherwise parks values in
+# AGPRs), unchanged on the larger shapes.
 SRC_FLAGS = {"fa_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+             "fa_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
              "fa_bwd_d64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 

@@ -1,8 +1,5 @@
-// Head-dimension 64 instantiation of the backward kernels (fa_bwd_kernels.h).
-// This source is compiled with the MFMA results kept in VGPRs
-// (-amdgpu-mfma-vgpr-form): at d = 64 the dK/dV kernel then needs no
-// AGPR<->VGPR copies and the backward runs 8-15% faster; at d = 128 the same
-// flag costs 2%, so fa_bwd.hip is compiled without it.
+// Head-dimension 64 instantiation of the backward kernels (fa_bwd_kernels.h),
+// in a source of its own so each head dimension compiles separately.
 #include "fa_bwd_kernels.h"
 
 namespace fa92 {

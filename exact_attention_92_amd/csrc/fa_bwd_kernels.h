@@ -1,7 +1,6 @@
 // Backward kernels of the exact attention library (gfx950 / MI355X), shared by
 // fa_bwd.hip (head dimension 128 and the fa_bwd entry point) and
-// fa_bwd_d64.hip (head dimension 64, compiled with MFMA results kept in
-// VGPRs, which is 8-15% faster there and 2% slower at d = 128).
+// fa_bwd_d64.hip (head dimension 64).
 //
 // The gradients are those of the section Backward为什么更复杂 of
 // "FlashAttention算法详解：从IO瓶颈到Triton实现" (gentlecold.top), with the
@@ -23,13 +22,14 @@
 //    consecutive registers are 8 consecutive keys), rebuilds P, forms dS and
 //    accumulates dQ^T += K^T dS^T with dS rounded to bf16 straight from the
 //    registers.  Its prologue computes D for its rows and writes it out.
-//  * fa_bwd_dkdv_kernel: keys outside, queries inside.  A wave owns 32 keys
-//    (their K and V rows stay in registers as MFMA operands); per block of 64
-//    query rows it computes S = Q K^T and dP = dO V^T with ONE KEY per lane,
-//    rebuilds P from the staged LSE, forms dS with the staged D, and
-//    accumulates dV^T += dO^T P and dK^T += Q^T dS.  Q and dO blocks are
-//    staged in LDS twice: row-major (operands of S and dP) and transposed
-//    (operands of dV^T and dK^T), from one set of global loads.
+//  * fa_bwd_dkdv_kernel: keys outside, queries inside.  A workgroup owns 128
+//    keys; two waves of a SIMD share 32 of them: one keeps their K rows in
+//    registers, computes S = Q K^T (one key per lane) per block of 64 query
+//    rows, rebuilds P from the staged LSE and accumulates dV^T += dO^T P; it
+//    hands P to the other through LDS, which keeps the V rows, computes
+//    dP = dO V^T, forms dS with the staged D and accumulates dK^T += Q^T dS.
+//    Q and dO are staged once, row-major; the transposed operands come from
+//    the transposing LDS read.  (Details above the kernel.)
 //
 // The second kernel reads the D written by the first, so both are enqueued,
 // in that order, on the caller's stream.
