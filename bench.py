@@ -85,6 +85,15 @@ def measured_traffic(which="fwd"):
     return rec.get("hbm_bytes_per_launch")
 
 
+def oracle_threads(cores, heads):
+    """Threads the oracle runs on: one worker per head (single-threaded BLAS)
+    up to ``cores``; a single head runs serially with BLAS's own threads."""
+    if heads > 1:
+        used = min(cores, heads)
+        return used, f"{used} worker threads with single-threaded BLAS"
+    return cores, f"one head, serial, BLAS threads (up to {cores})"
+
+
 def cpu_baseline(x, wl, o_gpu):
     """Time the oracle on the host (all heads of the workload) and check the
     GPU output against it on the same bytes."""
@@ -98,10 +107,11 @@ def cpu_baseline(x, wl, o_gpu):
     err = np.abs(o_gpu - Or)
     parity = {"o_max_abs": float(err.max()),
               "o_rel_frobenius": float(np.linalg.norm(o_gpu - Or) / np.linalg.norm(Or))}
-    return {"value": wl.flops() / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
+    used, how = oracle_threads(cores, wl.B * wl.H)
+    return {"value": wl.flops() / dt / 1e12, "unit": "TFLOP/s", "cores": used,
             "kind": "oracle", "seconds": round(dt, 3),
             "sample": f"the whole workload ({wl.B * wl.H} heads, all rows), fp64 NumPy/BLAS, "
-                      f"{cores} worker threads with single-threaded BLAS"}, parity
+                      f"{how}"}, parity
 
 
 def cpu_baseline_window(x, wl, o_gpu_rows, rows):
@@ -167,10 +177,11 @@ def cpu_baseline_bwd(x, wl, g):
     for name, want in zip(("dq", "dk", "dv"), ref[:3]):
         parity[f"{name}_rel_frobenius"] = float(np.linalg.norm(g[name] - want) /
                                                 np.linalg.norm(want))
-    return {"value": wl.bwd_flops() / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
+    used, how = oracle_threads(cores, wl.B * wl.H)
+    return {"value": wl.bwd_flops() / dt / 1e12, "unit": "TFLOP/s", "cores": used,
             "kind": "oracle", "seconds": round(dt, 3),
             "sample": f"the whole workload ({wl.B * wl.H} heads, all rows), fp64 NumPy/BLAS, "
-                      f"{cores} worker threads with single-threaded BLAS"}, parity
+                      f"{how}"}, parity
 
 
 def decode_bench(args):
