@@ -68,7 +68,10 @@ __device__ __forceinline__ i32x8_t join(u32x4_t lo, u32x4_t hi) {
 
 // Four floats (already scaled into [0, 448]) -> four E4M3 bytes, nearest even.
 __device__ __forceinline__ unsigned pack_fp8x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  // The first conversion writes the low half-word; the second the high one
+  // (the old-value operand of the first is never seen, so any register
+  // already holding a value does, without a move).
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
   return (unsigned)w;
 }
@@ -287,7 +290,7 @@ void fa_fwd_fp8_kernel(P8Params p) {
       // The row sum accumulates e.
       const float base = ((m_run == -INFINITY) ? 0.f : m_run) - kLog2PScale;
       i32x8_t pb[NSB];
-      float rs0 = 0.f, rs1 = 0.f;
+      float rs0, rs1;   // e >= 0: starting from the first pair sums is 0 + x exactly
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
@@ -296,8 +299,13 @@ void fa_fwd_fp8_kernel(P8Params p) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             e[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][4 * g + i], c, -base));
-          rs0 += e[0] + e[1];
-          rs1 += e[2] + e[3];
+          if (kt == 0 && g == 0) {
+            rs0 = e[0] + e[1];
+            rs1 = e[2] + e[3];
+          } else {
+            rs0 += e[0] + e[1];
+            rs1 += e[2] + e[3];
+          }
           pb[kt >> 1][4 * (kt & 1) + g] = (int)pack_fp8x4(e[0], e[1], e[2], e[3]);
         }
       l_run += rs0 + rs1;
