@@ -343,7 +343,7 @@ void fa_fwd_bf16_kernel(Params p) {
     // sums; the scores are left intact.
     auto exps = [&](const f32x16_t (&s)[KT], u32x4_t (&pb)[PC], float base, float& re,
                     float& rs) {
-      float re0 = 0.f, re1 = 0.f, rs0 = 0.f, rs1 = 0.f;
+      float re0, re1, rs0 = 0.f, rs1 = 0.f;   // p >= 0: the fp32 sums start at the first p
 #pragma unroll
       for (int pc = 0; pc < PC; ++pc) {
         const int kt = pc >> 1, r0 = 8 * (pc & 1);
@@ -351,8 +351,8 @@ void fa_fwd_bf16_kernel(Params p) {
         for (int w = 0; w < 4; ++w) {
           const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r0 + 2 * w], c, -base));
           const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r0 + 2 * w + 1], c, -base));
-          re0 += e0;
-          re1 += e1;
+          re0 = (pc == 0 && w == 0) ? e0 : re0 + e0;
+          re1 = (pc == 0 && w == 0) ? e1 : re1 + e1;
           pb[pc][w] = pack_bf16(e0, e1);
         }
         rs0 = sum_bf16x2(pb[pc][0], sum_bf16x2(pb[pc][1], rs0));
