@@ -176,10 +176,16 @@ void fa_bwd_dq_kernel(BwdParams p) {
   // Staging of key block j: pieces of 4 keys x 8 dims.  K goes to LDS
   // row-major and transposed, V row-major.  Buffer ranges end at the last
   // visible key, so hidden rows arrive as zeros (whatever memory holds).
+  // The piece's column chunk is rotated by rg/2: a 16-byte LDS store serves
+  // 8 lanes per cycle over 128 bytes of banks, and rows 4rg of 2d + 16 bytes
+  // start 64 (rg odd) or 0 bytes into those 128, so without the rotation 8
+  // consecutive lanes (rg = 0..7, same chunk) hit only two 16-byte positions.
+  // With it they cover all eight; the transposed 8-byte stores (16 lanes,
+  // 8rg bytes apart) stay conflict-free for any chunk.
   const int unit = SPLIT ? (tid < UNITS ? tid : tid - UNITS) : tid;
   const bool does_k = SPLIT ? tid < UNITS : true;
   const bool does_v = SPLIT ? (tid >= UNITS && tid < 2 * UNITS) : true;
-  const int rg = unit % (BN / 4), dc = unit / (BN / 4);
+  const int rg = unit % (BN / 4), dc = (unit / (BN / 4) + rg / 2) % CPR;
   const uint32_t u_off = (uint32_t)(4 * rg) * ROWB + 16u * dc;
   u32x4_t kreg[4], vreg[4];
   auto load_block = [&](int j) {
