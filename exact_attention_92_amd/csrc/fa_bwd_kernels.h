@@ -129,7 +129,7 @@ void fa_bwd_dq_kernel(BwdParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31;
   const int hf = lane >> 5;
   const bool causal = p.causal != 0;
@@ -182,15 +182,26 @@ void fa_bwd_dq_kernel(BwdParams p) {
   // consecutive lanes (rg = 0..7, same chunk) hit only two 16-byte positions.
   // With it they cover all eight; the transposed 8-byte stores (16 lanes,
   // 8rg bytes apart) stay conflict-free for any chunk.
+  // With SPLIT, whole waves stage K, the next ones V, through one register
+  // array (the choice is wave-uniform, so the buffer descriptor stays scalar).
+  static_assert(!SPLIT || UNITS % 64 == 0, "staging units per wave");
   const int unit = SPLIT ? (tid < UNITS ? tid : tid - UNITS) : tid;
-  const bool does_k = SPLIT ? tid < UNITS : true;
-  const bool does_v = SPLIT ? (tid >= UNITS && tid < 2 * UNITS) : true;
+  const bool does_k = SPLIT ? wave < UNITS / 64 : true;
+  const bool does_v = SPLIT ? (wave >= UNITS / 64 && wave < 2 * UNITS / 64) : true;
   const int rg = unit % (BN / 4), dc = (unit / (BN / 4) + rg / 2) % CPR;
   const uint32_t u_off = (uint32_t)(4 * rg) * ROWB + 16u * dc;
   u32x4_t kreg[4], vreg[4];
   auto load_block = [&](int j) {
     const int kbase = j * BN;
     const uint32_t bytes = (uint32_t)max(0, n_vis - kbase) * ROWB;
+    if (SPLIT) {
+      if (does_k || does_v) {
+        const rsrc_t r = make_rsrc((does_k ? Kh : Vh) + (size_t)kbase * D, bytes);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kreg[i] = buf_load16(r, u_off + i * ROWB);
+      }
+      return;
+    }
     if (does_k) {
       const rsrc_t rk = make_rsrc(Kh + (size_t)kbase * D, bytes);
 #pragma unroll
@@ -215,8 +226,9 @@ void fa_bwd_dq_kernel(BwdParams p) {
       }
     }
     if (does_v) {
+      const u32x4_t* src = SPLIT ? kreg : vreg;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) *(u32x4_t*)&v_lds[buf][4 * rg + i][8 * dc] = vreg[i];
+      for (int i = 0; i < 4; ++i) *(u32x4_t*)&v_lds[buf][4 * rg + i][8 * dc] = src[i];
     }
   };
 
@@ -225,6 +237,11 @@ void fa_bwd_dq_kernel(BwdParams p) {
   for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16();
   const float c = p.c;
   const int krow = row_perm(n);
+  // dP^T accumulators start from -D (every register of a lane belongs to its
+  // row), so they end as dP - D.
+  f32x16_t negd;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) negd[r] = -drow;
 
   if (nblk > 0) {
     load_block(0);
@@ -245,7 +262,7 @@ void fa_bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
         s[kt] = zero16();
-        dp[kt] = zero16();
+        dp[kt] = negd;
       }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
@@ -274,8 +291,7 @@ void fa_bwd_dq_kernel(BwdParams p) {
         for (int w = 0; w < 4; ++w) {
           const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r0 + 2 * w], c, -l2));
           const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r0 + 2 * w + 1], c, -l2));
-          dsb[pc][w] = pack_bf16(p0 * (dp[kt][r0 + 2 * w] - drow),
-                                 p1 * (dp[kt][r0 + 2 * w + 1] - drow));
+          dsb[pc][w] = pack_bf16(p0 * dp[kt][r0 + 2 * w], p1 * dp[kt][r0 + 2 * w + 1]);
         }
       }
       // dQ^T += K_j^T dS^T: A operand = K^T rows 32dt + n, keys 16pc + 8hf + 0..7.
