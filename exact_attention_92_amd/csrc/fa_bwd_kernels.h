@@ -256,52 +256,66 @@ void fa_bwd_dq_kernel(BwdParams p) {
     const int kbase = j * BN;
     const bool wave_skip = causal && (kbase > qw0 + 31);
     if (!wave_skip) {
-      // S^T = K_j Q^T and dP^T = V_j dO^T, key rows permuted: register r of
-      // tile kt holds key kbase + 32kt + 16(r/8) + 8hf + r%8.
+      // Per 32-key tile: S^T = K_j Q^T and dP^T = V_j dO^T (key rows permuted:
+      // register r of tile kt holds key kbase + 32kt + 16(r/8) + 8hf + r%8),
+      // P = 2^(s c - LSE2), dS = P (dP - D) packed to bf16 as dS^T chunks
+      // (chunk pc = registers 8(pc%2).. of tile pc/2 = keys 16pc + 8hf + 0..7),
+      // dQ^T += K_j^T dS^T.  Order: tile 0's products; tile 1's products beside
+      // tile 0's exponentials; tile 0's dQ products beside tile 1's
+      // exponentials; tile 1's dQ products.
       f32x16_t s[KT], dp[KT];
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
+      u32x4_t dsb[PC];
+      const bool edge = (causal && kbase + BN - 1 > qw0) || kbase + BN > n_vis;
+      const int lim = (causal ? min(qrow, n_vis - 1) : n_vis - 1) - kbase - 8 * hf;
+      auto products = [&](int kt) {
         s[kt] = zero16();
         dp[kt] = negd;
-      }
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
+        for (int ks = 0; ks < KS; ++ks) {
           const u32x4_t a = *(const u32x4_t*)&k_lds[buf][32 * kt + krow][16 * ks + 8 * hf];
           s[kt] = mfma_bf16(a, qr[ks], s[kt]);
           const u32x4_t a2 = *(const u32x4_t*)&v_lds[buf][32 * kt + krow][16 * ks + 8 * hf];
           dp[kt] = mfma_bf16(a2, dor[ks], dp[kt]);
         }
-      if ((causal && kbase + BN - 1 > qw0) || kbase + BN > n_vis) {
-        const int lim = (causal ? min(qrow, n_vis - 1) : n_vis - 1) - kbase - 8 * hf;
-#pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
+      };
+      auto mask = [&](int kt) {
+        if (edge) {
 #pragma unroll
           for (int r = 0; r < 16; ++r)
             if (32 * kt + 16 * (r >> 3) + (r & 7) > lim) s[kt][r] = -INFINITY;
-      }
-      // P = 2^(s c - LSE2); dS = P (dP - D), packed to bf16 as dS^T chunks
-      // (chunk pc = registers 8(pc%2).. of tile pc/2 = keys 16pc + 8hf + 0..7).
-      u32x4_t dsb[PC];
-#pragma unroll
-      for (int pc = 0; pc < PC; ++pc) {
-        const int kt = pc >> 1, r0 = 8 * (pc & 1);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r0 + 2 * w], c, -l2));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r0 + 2 * w + 1], c, -l2));
-          dsb[pc][w] = pack_bf16(p0 * dp[kt][r0 + 2 * w], p1 * dp[kt][r0 + 2 * w + 1]);
         }
-      }
-      // dQ^T += K_j^T dS^T: A operand = K^T rows 32dt + n, keys 16pc + 8hf + 0..7.
+      };
+      auto dstile = [&](int kt) {
 #pragma unroll
-      for (int pc = 0; pc < PC; ++pc)
+        for (int h = 0; h < 2; ++h) {
+          const int pc = 2 * kt + h, r0 = 8 * h;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const u32x4_t a = *(const u32x4_t*)&kt_lds[buf][32 * dt + n][16 * pc + 8 * hf];
-          acc[dt] = mfma_bf16(a, dsb[pc], acc[dt]);
+          for (int w = 0; w < 4; ++w) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r0 + 2 * w], c, -l2));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r0 + 2 * w + 1], c, -l2));
+            dsb[pc][w] = pack_bf16(p0 * dp[kt][r0 + 2 * w], p1 * dp[kt][r0 + 2 * w + 1]);
+          }
         }
+      };
+      auto dq = [&](int kt) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const int pc = 2 * kt + h;
+            const u32x4_t a = *(const u32x4_t*)&kt_lds[buf][32 * dt + n][16 * pc + 8 * hf];
+            acc[dt] = mfma_bf16(a, dsb[pc], acc[dt]);
+          }
+      };
+      static_assert(KT == 2, "two key tiles per block");
+      products(0);
+      mask(0);
+      products(1);
+      dstile(0);
+      mask(1);
+      dq(0);
+      dstile(1);
+      dq(1);
     }
     if (more) store_block(buf ^ 1);
     __syncthreads();
