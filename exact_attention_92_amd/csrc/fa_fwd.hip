@@ -582,7 +582,12 @@ void fa_fwd_d128_kernel(Params p) {
     const uint32_t ooff0 = (uint32_t)rowA * 256u + 8u * hf, ooff1 = ooff0 + 8192u;
     const uint32_t loff0 = hf ? kOutOfRange : (uint32_t)rowA * 4u;
     const uint32_t loff1 = hf ? kOutOfRange : (uint32_t)rowB * 4u;
-    const uint32_t nbytes = (uint32_t)N * 256u, vbytes = (uint32_t)n_vis * 256u;
+    // K and V ranges end at the item's last key block: the staging of the
+    // blocks after it (the loop stages two blocks ahead) reads out of range
+    // and lands zeros without touching memory.
+    const uint32_t nbytes = (uint32_t)N * 256u;
+    const uint32_t kbytes = (uint32_t)min(N, 64 * nblk) * 256u;
+    const uint32_t vbytes = (uint32_t)min(n_vis, 64 * nblk) * 256u;
     const uint32_t lbytes = (uint32_t)N * 4u;
 #ifdef FA_D128_DEBUG
 #ifdef FA_D128_PROFILE
@@ -601,7 +606,7 @@ void fa_fwd_d128_kernel(Params p) {
     asm volatile(
 #include FA_D128_BODY
         :
-        : [klo] "s"((uint32_t)ka), [khi] "s"((uint32_t)(ka >> 32)), [kbytes] "s"(nbytes),
+        : [klo] "s"((uint32_t)ka), [khi] "s"((uint32_t)(ka >> 32)), [kbytes] "s"(kbytes),
           [vlo] "s"((uint32_t)va), [vhi] "s"((uint32_t)(va >> 32)), [vbytes] "s"(vbytes),
           [qlo] "s"((uint32_t)qa), [qhi] "s"((uint32_t)(qa >> 32)), [qbytes] "s"(nbytes),
           [olo] "s"((uint32_t)oa), [ohi] "s"((uint32_t)(oa >> 32)),
